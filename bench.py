@@ -1,0 +1,162 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+
+One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_main,
+fa_backward_finish -- exactly what fa_backward runs) over one batch of the synthetic workload,
+inputs resident in HBM.  W untimed steps, then K timed steps bracketed by synchronisation and
+HIP events on the stream the kernels run on; per-stage HIP events inside the timed region give the
+average duration of each kernel launch.
+
+FLOPs are algorithmic: forward 4 d per visible (query, key) pair (QK^T and PV), backward 2.5x
+forward (QK^T recomputed, dO V^T, P^T dO, dS^T Q, dS K).  Causal pairs per head N(N+1)/2.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (bf16, causal, N=4096 d=128) and % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs(N: int, causal: bool, key_len: int) -> int:
+    """(query, key) pairs with key < key_len and, if causal, key <= query."""
+    L = max(0, min(N, key_len))
+    if not causal:
+        return N * L
+    return L * (L + 1) // 2 + (N - L) * L
+
+
+def workload_flops(w, x):
+    lens = [w.N] * w.B if x["seqlens"] is None else [int(s) for s in x["seqlens"]]
+    pairs = sum(visible_pairs(w.N, w.causal, L) for L in lens) * w.H
+    fwd = 4.0 * w.d * pairs
+    return fwd, 2.5 * fwd
+
+
+def cpu_baseline(w, x, target_s: float = 12.0):
+    """Time the fp64 oracle (forward + backward) on the first heads of batch element 0."""
+    import torch
+
+    import oracle
+    sl = None if x["seqlens"] is None else x["seqlens"][:1]
+    # Without key padding every (batch, head) pair is alike: view them as heads of one batch element.
+    flat = {n: (x[n][:1] if sl is not None else x[n].reshape(1, w.B * w.H, w.N, w.d)) for n in ("q", "k", "v", "do")}
+    nmax = flat["q"].shape[1]
+
+    def run(nh):
+        sub = {n: flat[n][:, :nh].contiguous() for n in ("q", "k", "v", "do")}
+        t0 = time.perf_counter()
+        oracle.forward(sub["q"], sub["k"], sub["v"], x["scale"], w.causal, sl)
+        oracle.backward(sub["q"], sub["k"], sub["v"], sub["do"], x["scale"], w.causal, sl)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nh = int(max(1, min(nmax, target_s // max(t1, 1e-3))))
+    t = run(nh) if nh > 1 else t1
+    L = w.N if sl is None else int(sl[0])
+    flops = 4.0 * w.d * visible_pairs(w.N, w.causal, L) * nh * 3.5
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of the first {nh} of the {w.B * w.H} (batch, head) pairs, "
+                      f"{t:.1f} s wall; algorithmic FLOPs as for the GPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the attention of one "
+              f"(batch, head) never crosses GPUs and no multi-GPU path exists", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_66_amd as fa
+    import workloads
+
+    fa.load()
+    w = workloads.WORKLOADS[args.workload]
+    x = workloads.draw(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    sl = None if x["seqlens"] is None else x["seqlens"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    scale, causal = x["scale"], w.causal
+    flops_fwd, flops_bwd = workload_flops(w, x)
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
+        if e: e[1].record(stream)
+        fa.fa_backward_prepare(o, do, ws)
+        if e: e[2].record(stream)
+        fa.fa_backward_main(q, k, v, do, lse, dq, dk, dv, scale, causal, sl, ws)
+        if e: e[3].record(stream)
+        fa.fa_backward_finish(dq, scale, ws)
+        if e: e[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in ev) / args.steps
+
+    ms_fwd, ms_pre, ms_main, ms_fin = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    ms_bwd = ms_pre + ms_main + ms_fin
+    value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    kernels = {"fwd_bf16_kernel": (ms_fwd, flops_fwd), "bwd_main_kernel": (ms_main, flops_bwd)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_flops = kernels[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "key_padding": w.padded, "q_std": w.q_std, "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+                "pct_of_mfma_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "bwd": {"ms": round(ms_bwd, 4), "ms_prepare": round(ms_pre, 4), "ms_main": round(ms_main, 4),
+                "ms_finish": round(ms_fin, 4), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
+        "flops": {"fwd": flops_fwd, "bwd": flops_bwd},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "ms_per_launch": round(dom_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

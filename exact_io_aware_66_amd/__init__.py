@@ -1,0 +1,199 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library (C ABI in include/fa.h).
+
+Argument marshalling only: every step of the attention path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no fallback: if the library is
+missing or a call is unsupported, these functions raise.
+
+    fa_forward(q, k, v, o, lse, scale, causal, seqlens)            # C-ABI names, caller-owned outputs
+    fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace)
+    fa_backward_workspace_size(B, H, N, d, dtype)
+    forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
+    backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+FA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_MISALIGNED",
+          4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
+EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_main",
+           "fa_backward_finish", "fa_status_string", "fa_last_error")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libfa.so once and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run exact_io_aware_66_amd/build.py (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_backward.restype = i
+    lib.fa_backward_prepare.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_backward_prepare.restype = i
+    lib.fa_backward_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_backward_main.restype = i
+    lib.fa_backward_finish.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_backward_finish.restype = i
+    lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_backward_workspace_size.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FA_OK:
+        lib = load()
+        raise FAError(status, (lib.fa_last_error() or b"").decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dims(q):
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _dtype_code(t):
+    if t.dtype not in FA_DTYPE:
+        raise FAError(2, f"dtype {t.dtype} is not supported (float32 or bfloat16 only)")
+    return FA_DTYPE[t.dtype]
+
+
+def _same(ref, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        if t.device != ref.device:
+            raise ValueError("tensors must be on one device")
+
+
+def _seqlens(seqlens, B, device):
+    if seqlens is None:
+        return None
+    if not (seqlens.is_cuda and seqlens.dtype == torch.int32 and seqlens.numel() == B and seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 device tensor with B entries")
+    if seqlens.device != device:
+        raise ValueError("seqlens must be on the tensors' device")
+    return seqlens
+
+
+def fa_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
+    code = FA_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().fa_backward_workspace_size(B, H, N, d, code))
+
+
+def fa_forward(q, k, v, o, lse, scale: float, causal: bool = False, seqlens=None, stream=None) -> None:
+    """C-ABI fa_forward on caller-owned tensors (o: like q; lse: float32 [B, H, N])."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, lse)
+    seqlens = _seqlens(seqlens, B, q.device)
+    _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                          _ptr(seqlens), _dtype_code(q), _stream(stream)))
+
+
+def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, seqlens=None, workspace=None,
+                stream=None) -> None:
+    """C-ABI fa_backward on caller-owned tensors; `workspace` is a uint8 device tensor."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                           B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
+                           _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_backward_prepare(o, do, workspace, stream=None) -> None:
+    """Stage 1 of fa_backward: D = rowsum(dO * O) into the workspace; clears the dQ accumulator."""
+    lib = load()
+    B, H, N, d = _dims(o)
+    _same(o, do, workspace)
+    _check(lib.fa_backward_prepare(_ptr(o), _ptr(do), B, H, N, d, _dtype_code(o), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fa_backward_main(q, k, v, do, lse, dq, dk, dv, scale: float, causal: bool = False, seqlens=None,
+                     workspace=None, stream=None) -> None:
+    """Stage 2 of fa_backward: the recompute pass (dK, dV, dQ accumulation)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, do, lse, dq, dk, dv, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
+                                _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_backward_finish(dq, scale: float, workspace, stream=None) -> None:
+    """Stage 3 of fa_backward (bf16): dq = scale * accumulator."""
+    lib = load()
+    B, H, N, d = _dims(dq)
+    _same(dq, workspace)
+    _check(lib.fa_backward_finish(_ptr(dq), B, H, N, d, float(scale), _dtype_code(dq), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def _default_scale(d: int) -> float:
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=None, stream=None):
+    """Allocate O and LSE and run fa_forward; returns (o, lse)."""
+    B, H, N, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_forward(q, k, v, o, lse, scale, causal, seqlens, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, seqlens=None, stream=None,
+             workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_backward; returns (dq, dk, dv)."""
+    B, H, N, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(fa_backward_workspace_size(B, H, N, d, q.dtype), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace, stream)
+    return dq, dk, dv

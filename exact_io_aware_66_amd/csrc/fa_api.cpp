@@ -1,0 +1,237 @@
+// C-ABI entry points of the attention library (declared in include/fa.h): argument validation,
+// workspace sizing, dispatch to the compiled kernel specialisations, and error reporting.
+// Nothing here allocates device memory, and every argument error is reported before any work
+// is enqueued.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status_t fail(fa_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status_t fail(fa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(FA_ERR_HIP, "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxGridYZ = 65535;
+
+fa_status_t check_common(int B, int H, int N, int d, float scale, fa_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || N <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "B, H and N must be positive (got %d, %d, %d)", B, H, N);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not supported (only FA_DTYPE_F32 and FA_DTYPE_BF16)", (int)dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d is not supported (only 64 and 128)", d);
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return fail(FA_ERR_INVALID_ARGUMENT, "B and H must be at most %d", kMaxGridYZ);
+  return FA_OK;
+}
+
+fa_status_t check_tensor(const void* p, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(FA_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+fa_status_t check_f32_vec(const void* p, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, 4)) return fail(FA_ERR_MISALIGNED, "%s is not 4-byte aligned", name);
+  return FA_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace fa {
+BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d, bool bf16) {
+  BwdWorkspace w{};
+  const size_t rows = (size_t)B * H * N;
+  w.delta_off = 0;
+  w.delta_bytes = rows * sizeof(float);
+  w.dqacc_off = round_up(w.delta_bytes);
+  w.dqacc_bytes = bf16 ? rows * (size_t)d * sizeof(float) : 0;
+  w.total = w.dqacc_off + round_up(w.dqacc_bytes);
+  return w;
+}
+}  // namespace fa
+
+namespace {
+
+fa_status_t check_workspace(int B, int H, int N, int d, fa_dtype_t dtype, void* workspace, size_t workspace_bytes) {
+  const size_t need = fa_backward_workspace_size(B, H, N, d, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                need);
+  if (!aligned(workspace, 16)) return fail(FA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return FA_OK;
+}
+
+fa_status_t check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return FA_OK;
+}
+
+fa_status_t validate_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
+                             void* workspace, size_t workspace_bytes) {
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, 0.f, dtype)) != FA_OK) return s;
+  if ((s = check_tensor(o, "o")) != FA_OK || (s = check_tensor(dO, "dO")) != FA_OK) return s;
+  return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
+}
+
+fa_status_t validate_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
+                          void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens,
+                          fa_dtype_t dtype, void* workspace, size_t workspace_bytes) {
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
+  if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
+      (s = check_tensor(dO, "dO")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK ||
+      (s = check_tensor(dq, "dq")) != FA_OK || (s = check_tensor(dk, "dk")) != FA_OK ||
+      (s = check_tensor(dv, "dv")) != FA_OK)
+    return s;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
+  return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
+}
+
+fa_status_t validate_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes) {
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
+  if ((s = check_tensor(dq, "dq")) != FA_OK) return s;
+  return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
+}
+
+fa::Problem problem(int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens, void* stream) {
+  return fa::Problem{B, H, N, d, scale, causal != 0, seqlens, (hipStream_t)stream};
+}
+
+fa_status_t run_prepare(const fa::Problem& p, fa_dtype_t dtype, const void* o, const void* dO, void* workspace) {
+  hipError_t e = fa::launch_bwd_prepare(p, dtype == FA_DTYPE_BF16, o, dO, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward prepare launch");
+}
+
+fa_status_t run_main(const fa::Problem& p, fa_dtype_t dtype, const void* q, const void* k, const void* v,
+                     const void* dO, const float* lse, void* dq, void* dk, void* dv, void* workspace) {
+  hipError_t e = (dtype == FA_DTYPE_BF16)
+                     ? fa::launch_bwd_main_bf16(p, q, k, v, dO, lse, dk, dv, workspace)
+                     : fa::launch_bwd_main_f32(p, (const float*)q, (const float*)k, (const float*)v, (const float*)dO,
+                                               lse, (float*)dq, (float*)dk, (float*)dv, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward main launch");
+}
+
+fa_status_t run_finish(const fa::Problem& p, fa_dtype_t dtype, void* dq, void* workspace) {
+  if (dtype != FA_DTYPE_BF16) return FA_OK;
+  hipError_t e = fa::launch_bwd_finish_bf16(p, dq, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward finish launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d, fa_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128) || (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16)) return 0;
+  return fa::bwd_workspace_layout(B, H, N, d, dtype == FA_DTYPE_BF16).total;
+}
+
+fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                       float scale, int causal, const int32_t* seqlens, fa_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
+  if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
+      (s = check_tensor(o, "o")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK)
+    return s;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
+  if ((s = check_device()) != FA_OK) return s;
+  const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  const hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, q, k, v, o, lse)
+                               : fa::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse);
+  if (e != hipSuccess) return hip_fail(e, "fa_forward launch");
+  return FA_OK;
+}
+
+
+fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                        void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                        const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = validate_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, workspace,
+                         workspace_bytes)) != FA_OK)
+    return s;
+  if ((s = check_tensor(o, "o")) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  if ((s = run_prepare(p, dtype, o, dO, workspace)) != FA_OK) return s;
+  if ((s = run_main(p, dtype, q, k, v, dO, lse, dq, dk, dv, workspace)) != FA_OK) return s;
+  return run_finish(p, dtype, dq, workspace);
+}
+
+fa_status_t fa_backward_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = validate_prepare(o, dO, B, H, N, d, dtype, workspace, workspace_bytes)) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  return run_prepare(problem(B, H, N, d, 1.f, 0, nullptr, stream), dtype, o, dO, workspace);
+}
+
+fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
+                             void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                             const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = validate_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, workspace,
+                         workspace_bytes)) != FA_OK)
+    return s;
+  if ((s = check_device()) != FA_OK) return s;
+  return run_main(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dq, dk, dv, workspace);
+}
+
+fa_status_t fa_backward_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = validate_finish(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes)) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  return run_finish(problem(B, H, N, d, scale, 0, nullptr, stream), dtype, dq, workspace);
+}
+
+}  // extern "C"

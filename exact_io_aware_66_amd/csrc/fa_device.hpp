@@ -1,0 +1,149 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Everything here is specific to CDNA4 (gfx950): wave64, the bf16 matrix-core instruction
+// v_mfma_f32_32x32x16_bf16, the transposing LDS read ds_read_b64_tr_b16 and the direct
+// global->LDS load global_load_lds_dwordx4.
+//
+// Lane layouts used by the kernels (wave64, lane l, half h = l / 32):
+//   32x32x16 MFMA  A[32][16]: lane l holds row l%32, k = 8h .. 8h+7
+//                  B[16][32]: lane l holds column l%32, k = 8h .. 8h+7
+//                  C[32][32]: lane l holds column l%32, rows 8(r/4) + 4h + r%4 for r = 0..15
+//   ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i%4 of the 8-byte rows
+//                  addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its group.
+//   global_load_lds_dwordx4: lane i of a wave writes its 16 bytes at LDS base + 16 i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// XOR swizzle of the 16-byte chunk index inside one LDS row, keyed by the row.  Any 8 consecutive
+// rows read at the same logical chunk land on 8 different chunk positions (conflict-free 128-bit
+// reads), and any 4 consecutive rows starting at a multiple of 4 keep each aligned pair of chunks
+// together while moving the pairs apart (conflict-free transposing 64-bit reads).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Byte offset of (row, element col) in a row-major LDS tile of `ncol` bf16 per row, swizzled.
+template <int NCOL>
+__device__ __forceinline__ uint32_t tile_off(int row, int col) {
+  const int c = col >> 3;
+  return (uint32_t)(row * (NCOL * 2) + ((c ^ swz(row)) << 4) + ((col & 7) << 1));
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const FA_LDS char* base, uint32_t off) {
+  return *(const FA_LDS bf16x8*)(base + off);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const FA_LDS char* base, uint32_t off) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + off));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// The same transposing read issued through inline assembly.  The compiler then does not treat it as
+// an LDS load that may alias an in-flight direct global->LDS prefetch (for the builtin it inserts a
+// full vmcnt wait, serialising the prefetch); the caller must wait for the result with
+// lds_wait() before using it.  `addr` is the byte address inside LDS.
+template <int OFFSET = 0>
+__device__ __forceinline__ u32x2 lds_read_tr_asm(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
+  return r;
+}
+
+// Wait for every outstanding LDS access of this wave; the listed values become dependent on the
+// wait so their uses cannot be scheduled above it.
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f, u32x2& g,
+                                         u32x2& h) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const FA_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 cat(u32x2 a, u32x2 b) {
+  return cat(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b));
+}
+
+// 16 bytes from global memory straight into LDS at (wave-uniform) lds_base + 16 * lane.
+__device__ __forceinline__ void gload_lds16(const void* gptr, FA_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+}
+// 4 bytes from global memory into LDS at (wave-uniform) lds_base + 4 * lane.
+__device__ __forceinline__ void gload_lds4(const void* gptr, FA_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Value of x in lane l ^ 32 combined with x by max / add (one v_permlane32_swap).
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float min_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 8 consecutive fp32 accumulator values -> 8 bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  f32x2 a = {s[base + 0], s[base + 1]}, b = {s[base + 2], s[base + 3]};
+  f32x2 c = {s[base + 4], s[base + 5]}, d = {s[base + 6], s[base + 7]};
+  bf16x2 pa = __builtin_convertvector(a, bf16x2), pb = __builtin_convertvector(b, bf16x2);
+  bf16x2 pc = __builtin_convertvector(c, bf16x2), pd = __builtin_convertvector(d, bf16x2);
+  bf16x4 lo = __builtin_shufflevector(pa, pb, 0, 1, 2, 3);
+  bf16x4 hi = __builtin_shufflevector(pc, pd, 0, 1, 2, 3);
+  return cat(lo, hi);
+}
+
+__device__ __forceinline__ bf16x4 pack4(float a0, float a1, float a2, float a3) {
+  f32x2 a = {a0, a1}, b = {a2, a3};
+  bf16x2 pa = __builtin_convertvector(a, bf16x2), pb = __builtin_convertvector(b, bf16x2);
+  return __builtin_shufflevector(pa, pb, 0, 1, 2, 3);
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
+  int L = seqlens[b];
+  return L < 0 ? 0 : (L > N ? N : L);
+}
+
+}  // namespace fa

@@ -1,0 +1,134 @@
+/*
+ * fa.h -- C ABI of the exact, tiled, fused attention library for AMD MI355X (gfx950).
+ *
+ * What is computed
+ *   For every batch element b and head h, with Q, K, V the N x d matrices of that head:
+ *     S   = scale * Q K^T + mask                       (mask entries are 0 or -inf)
+ *     O   = softmax_rows(S) V
+ *     LSE = per-row natural-log log-sum-exp of S      (the statistic the backward reuses)
+ *   "NOTE-005: FlashAttention" (anthology-of-the-sota), section "Key results", Theorem 1 states
+ *   the product softmax(Q K^T) V; the scaling and masking steps come from the promptingindex page
+ *   "FlashAttention: The IO-Aware Algorithm That Rewrote GPU Training Speed Records", section
+ *   "Why attention is memory-bound, not compute-bound".  The forward keeps a running maximum and
+ *   normaliser per row and stores LSE = m + ln(l); the backward recomputes the attention block
+ *   from it instead of reading a stored N x N matrix (NOTE-005, "Method").  The N x N score matrix
+ *   never exists in device memory.
+ *
+ * Masks
+ *   causal != 0 : key j is visible to query i only if j <= i (top-left aligned; queries and keys
+ *                 have the same length N).
+ *   seqlens     : optional device array of B int32 valid key counts.  Key j of batch element b is
+ *                 visible only if j < clamp(seqlens[b], 0, N), for every head and every query.
+ *                 Query rows at or past that length are still computed (they attend to the valid
+ *                 keys).  A row with no visible key gets O = 0, LSE = -inf and no gradient.
+ *   Both masks combine by AND.  There is no dropout.
+ *
+ * Layout and types (all tensors are caller-owned device memory)
+ *   q, k, v, o, dO, dq, dk, dv : contiguous row-major [B][H][N][d], d fastest, element type `dtype`.
+ *   lse                        : contiguous [B][H][N] float32 (natural log, units of the scaled
+ *                                scores), written by fa_forward and read by fa_backward.
+ *   d must be 64 or 128.  Any N >= 1 (ragged tails are masked); offsets are 64-bit.
+ *   Base pointers of the [B][H][N][d] tensors must be 16-byte aligned, lse and seqlens 4-byte.
+ *   bf16 results are rounded to nearest even; every accumulation is float32.
+ *
+ * Ownership, threads, streams
+ *   The library allocates nothing and keeps no state between calls (apart from a thread-local
+ *   error string).  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and runs
+ *   asynchronously; a return of FA_OK means the work was enqueued.  Outputs must not alias
+ *   inputs.  Calls from several host threads are safe.
+ *
+ * Errors
+ *   Argument errors are detected on the host before anything is enqueued; outputs are then left
+ *   untouched.  A kernel fault surfaces at the caller's next synchronisation, like any HIP error.
+ *   No call prints, throws or aborts.  There is no fallback path: an unsupported dtype or head
+ *   dimension is an error (FA_ERR_UNSUPPORTED), never a silent switch to another attention.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N <= 0, non-finite scale, grid too large */
+  FA_ERR_UNSUPPORTED = 2,      /* dtype not FA_DTYPE_F32/FA_DTYPE_BF16, or d not 64/128 */
+  FA_ERR_MISALIGNED = 3,       /* a base pointer breaks the alignment rule above */
+  FA_ERR_WORKSPACE = 4,        /* workspace null or smaller than fa_backward_workspace_size() */
+  FA_ERR_HIP = 5               /* the HIP runtime reported an error (text in fa_last_error()) */
+} fa_status_t;
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+
+/*
+ * Forward: O and LSE (see above).
+ *   q, k, v : inputs [B][H][N][d]             o   : output [B][H][N][d]
+ *   lse     : output [B][H][N] float32        scale: multiplies Q K^T (usually 1/sqrt(d))
+ *   causal  : 0 or 1                          seqlens: device int32[B] or NULL
+ * Extra device memory: none.  The tile loop (the pages' tiling of Q, K and V into on-chip blocks
+ * with online softmax; NOTE-005 "Method") runs entirely in LDS and registers.
+ */
+fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const int32_t* seqlens, fa_dtype_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_backward needs for these sizes: one float32 per row for
+ * D_i = sum_c dO_ic O_ic, plus (bf16 only) a float32 [B][H][N][d] accumulator for dQ.
+ * Returns 0 for invalid or unsupported sizes.  Linear in N (O(N) extra memory; NOTE-005 "Key
+ * results", Theorem 1).
+ */
+size_t fa_backward_workspace_size(int B, int H, int N, int d, fa_dtype_t dtype);
+
+/*
+ * Backward of the loss sum(dO * O): writes dq, dk, dv ([B][H][N][d], element type dtype).
+ *   o, lse must be exactly what fa_forward returned for the same q, k, v, sizes, scale, causal
+ *   and seqlens (not checked; otherwise the result is undefined).
+ *   workspace: caller-owned device memory of at least fa_backward_workspace_size() bytes,
+ *   16-byte aligned; the library clears what it needs itself.  Its contents are scratch.
+ * The attention block is recomputed from Q, K and LSE (NOTE-005 "Method"); dQ is accumulated
+ * across key blocks with float32 atomic adds, so its last bits may differ between runs, while
+ * dk and dv are bitwise reproducible.
+ */
+fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const int32_t* seqlens, fa_dtype_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward in its three stages, for callers that schedule or time them separately.
+ * fa_backward(...) is exactly these three calls in order on one stream, with the same workspace:
+ *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; clears the dQ accumulator
+ *                         (bf16).  Reads o and dO only.
+ *   fa_backward_main    : the recompute pass over key blocks: writes dk, dv, and accumulates dQ
+ *                         (bf16: into the workspace; float32: straight into dq).  Needs the
+ *                         workspace as fa_backward_prepare left it.
+ *   fa_backward_finish  : bf16 only: dq = scale * (dQ accumulator), rounded to bf16.  No work for
+ *                         float32 (returns FA_OK).
+ * Arguments, layout and errors as in fa_backward.
+ */
+fa_status_t fa_backward_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                             void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                             int causal, const int32_t* seqlens, fa_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+fa_status_t fa_backward_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* fa_status_string(fa_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,103 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol include/fa.h declares,
+and every argument error is reported on the host, before any device call, with its status code.
+
+Pointers passed here are fake (never dereferenced): validation rejects them or, when every
+argument is valid, the first HIP call reports the missing device as FA_ERR_HIP.  On a machine
+with a GPU the valid-argument case is skipped (it would launch on garbage pointers).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_66_amd as fa
+from conftest import gpu_available
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
+F32, BF16 = 0, 1
+P = 0x7F0000000000  # 16-byte aligned fake device address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+char\s*\*|fa_status_t|size_t)\s+(fa_\w+)\s*\(", text, re.M))
+    assert declared == set(fa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in fa.STATUS.items():
+        assert lib.fa_status_string(code).decode() == name
+    assert lib.fa_status_string(99).decode() == "FA_ERR_UNKNOWN"
+
+
+def _fwd(lib, q=P, k=P + 4096, v=P + 8192, o=P + 12288, lse=P + 16384, B=2, H=3, N=100, d=64, scale=0.125,
+         causal=0, seqlens=None, dtype=BF16):
+    return lib.fa_forward(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, dtype, None)
+
+
+def _bwd(lib, ws=P + 65536, ws_bytes=None, B=2, H=3, N=100, d=64, dtype=BF16, scale=0.125, dq=P + 20480, lse=P + 16384,
+         seqlens=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_backward_workspace_size(B, H, N, d, dtype)
+    return lib.fa_backward(P, P + 4096, P + 8192, P + 12288, P + 24576, lse, dq, P + 28672, P + 32768,
+                           B, H, N, d, scale, 1, seqlens, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(B=70000), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
+    (dict(q=P + 8), MISALIGNED), (dict(o=P + 2), MISALIGNED), (dict(lse=P + 2), MISALIGNED),
+    (dict(seqlens=P + 1), MISALIGNED),
+])
+def test_forward_argument_errors(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 65536 + 4), MISALIGNED),
+    (dict(dq=None), INVALID), (dict(dq=P + 4), MISALIGNED), (dict(lse=None), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(N=-5), INVALID), (dict(scale=float("nan")), INVALID), (dict(seqlens=P + 2), MISALIGNED),
+])
+def test_backward_argument_errors(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def test_workspace_size_is_linear_in_n(lib):
+    sizes = [lib.fa_backward_workspace_size(2, 16, n, 128, BF16) for n in (1024, 2048, 4096)]
+    assert sizes[1] > sizes[0] > 0 and sizes[2] - sizes[1] == 2 * (sizes[1] - sizes[0])
+    # bf16: fp32 D row statistic + fp32 dQ accumulator; fp32 inputs: the row statistic only
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, BF16) >= 2 * 16 * 4096 * (4 + 128 * 4)
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, F32) >= 2 * 16 * 4096 * 4
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, F32) < 2 * 16 * 4096 * 8
+    assert lib.fa_backward_workspace_size(0, 16, 4096, 128, BF16) == 0
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 96, BF16) == 0
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, 7) == 0
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_valid_arguments_without_device_report_hip_error(lib):
+    assert _fwd(lib) == HIP
+    assert "hipGetDevice" in lib.fa_last_error().decode()
+    assert _bwd(lib) == HIP
+
+
+def test_python_binding_rejects_unsupported_dtype_without_fallback():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(fa.FAError) as ei:
+        fa._dtype_code(q)
+    assert ei.value.status == UNSUPPORTED
