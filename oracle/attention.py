@@ -187,12 +187,14 @@ def backward_rows(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: i
     return torch.matmul(p * (dp - D), kh) * float(scale)
 
 
-def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, chunk: int = 1024):
+def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, chunk: int = 1024,
+              progress=None):
     """LSE_i and D_i for every row of head (b, h), computed ``chunk`` complete rows at a time.
 
     D_i = sum_j P_ij dP_ij is evaluated as dO_i . O_i, which equals it because
     dP_ij = dO_i . v_j and O_i = sum_j P_ij v_j (the identity is checked against
-    ``backward`` in the oracle's own tests).
+    ``backward`` in the oracle's own tests).  ``progress(done_rows, N)`` is
+    called after each chunk when given (long passes report that they are alive).
     """
     N = q.shape[2]
     lse = torch.empty(N, dtype=F64)
@@ -203,6 +205,8 @@ def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, 
         o_r, lse_r = forward_rows(q, k, v, scale, causal, seqlens, b, h, rows)
         lse[rows] = lse_r
         D[rows] = torch.sum(o_r * doh[rows], dim=1)
+        if progress is not None:
+            progress(int(rows[-1]) + 1, N)
     return lse, D
 
 
