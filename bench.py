@@ -108,7 +108,7 @@ def main():
         if e: e[0].record(stream)
         fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
         if e: e[1].record(stream)
-        fa.fa_backward_prepare(o, do, ws)
+        fa.fa_backward_prepare(o, do, lse, ws)
         if e: e[2].record(stream)
         fa.fa_backward_main(q, k, v, do, lse, dq, dk, dv, scale, causal, sl, ws)
         if e: e[3].record(stream)

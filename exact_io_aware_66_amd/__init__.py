@@ -50,7 +50,7 @@ def load(path: str = LIB_PATH):
     lib.fa_forward.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
     lib.fa_backward.restype = i
-    lib.fa_backward_prepare.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_backward_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_backward_prepare.restype = i
     lib.fa_backward_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
     lib.fa_backward_main.restype = i
@@ -142,12 +142,12 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fa
                            _ptr(workspace), nbytes, _stream(stream)))
 
 
-def fa_backward_prepare(o, do, workspace, stream=None) -> None:
-    """Stage 1 of fa_backward: D = rowsum(dO * O) into the workspace; clears the dQ accumulator."""
+def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
+    """Stage 1 of fa_backward: D = rowsum(dO * O) (bf16: also LSE log2 e and a cleared dQ accumulator)."""
     lib = load()
     B, H, N, d = _dims(o)
-    _same(o, do, workspace)
-    _check(lib.fa_backward_prepare(_ptr(o), _ptr(do), B, H, N, d, _dtype_code(o), _ptr(workspace),
+    _same(o, do, lse, workspace)
+    _check(lib.fa_backward_prepare(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _dtype_code(o), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

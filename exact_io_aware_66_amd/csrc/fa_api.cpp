@@ -66,8 +66,10 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d, bool bf16) {
   const size_t rows = (size_t)B * H * N;
   w.delta_off = 0;
   w.delta_bytes = rows * sizeof(float);
-  w.dqacc_off = round_up(w.delta_bytes);
-  w.dqacc_bytes = bf16 ? rows * (size_t)d * sizeof(float) : 0;
+  w.lse2_off = round_up(w.delta_bytes);
+  w.lse2_bytes = bf16 ? rows * sizeof(float) : 0;
+  w.dqacc_off = w.lse2_off + round_up(w.lse2_bytes);
+  w.dqacc_bytes = bf16 ? (size_t)B * H * bwd_rows_padded(N) * (size_t)d * sizeof(float) : 0;
   w.total = w.dqacc_off + round_up(w.dqacc_bytes);
   return w;
 }
@@ -91,11 +93,13 @@ fa_status_t check_device() {
   return FA_OK;
 }
 
-fa_status_t validate_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
-                             void* workspace, size_t workspace_bytes) {
+fa_status_t validate_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                             fa_dtype_t dtype, void* workspace, size_t workspace_bytes) {
   fa_status_t s;
   if ((s = check_common(B, H, N, d, 0.f, dtype)) != FA_OK) return s;
-  if ((s = check_tensor(o, "o")) != FA_OK || (s = check_tensor(dO, "dO")) != FA_OK) return s;
+  if ((s = check_tensor(o, "o")) != FA_OK || (s = check_tensor(dO, "dO")) != FA_OK ||
+      (s = check_f32_vec(lse, "lse")) != FA_OK)
+    return s;
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
@@ -110,6 +114,8 @@ fa_status_t validate_main(const void* q, const void* k, const void* v, const voi
       (s = check_tensor(dv, "dv")) != FA_OK)
     return s;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
+  if (dtype == FA_DTYPE_BF16 && fa::bwd_bf16_grid(B, H, N) > 0x7fffffff)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
@@ -125,15 +131,16 @@ fa::Problem problem(int B, int H, int N, int d, float scale, int causal, const i
   return fa::Problem{B, H, N, d, scale, causal != 0, seqlens, (hipStream_t)stream};
 }
 
-fa_status_t run_prepare(const fa::Problem& p, fa_dtype_t dtype, const void* o, const void* dO, void* workspace) {
-  hipError_t e = fa::launch_bwd_prepare(p, dtype == FA_DTYPE_BF16, o, dO, workspace);
+fa_status_t run_prepare(const fa::Problem& p, fa_dtype_t dtype, const void* o, const void* dO, const float* lse,
+                        void* workspace) {
+  hipError_t e = fa::launch_bwd_prepare(p, dtype == FA_DTYPE_BF16, o, dO, lse, workspace);
   return e == hipSuccess ? FA_OK : hip_fail(e, "backward prepare launch");
 }
 
 fa_status_t run_main(const fa::Problem& p, fa_dtype_t dtype, const void* q, const void* k, const void* v,
                      const void* dO, const float* lse, void* dq, void* dk, void* dv, void* workspace) {
   hipError_t e = (dtype == FA_DTYPE_BF16)
-                     ? fa::launch_bwd_main_bf16(p, q, k, v, dO, lse, dk, dv, workspace)
+                     ? fa::launch_bwd_main_bf16(p, q, k, v, dO, dk, dv, workspace)
                      : fa::launch_bwd_main_f32(p, (const float*)q, (const float*)k, (const float*)v, (const float*)dO,
                                                lse, (float*)dq, (float*)dk, (float*)dv, workspace);
   return e == hipSuccess ? FA_OK : hip_fail(e, "backward main launch");
@@ -178,6 +185,8 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
     return s;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
   if ((s = check_device()) != FA_OK) return s;
+  if (dtype == FA_DTYPE_BF16 && fa::fwd_bf16_grid(B, H, N) > 0x7fffffff)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/256) must be below 2^31");
   const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   const hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, q, k, v, o, lse)
                                : fa::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse);
@@ -198,18 +207,18 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
   if ((s = check_tensor(o, "o")) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
   const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
-  if ((s = run_prepare(p, dtype, o, dO, workspace)) != FA_OK) return s;
+  if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
   if ((s = run_main(p, dtype, q, k, v, dO, lse, dq, dk, dv, workspace)) != FA_OK) return s;
   return run_finish(p, dtype, dq, workspace);
 }
 
-fa_status_t fa_backward_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                                fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   fa_status_t s;
-  if ((s = validate_prepare(o, dO, B, H, N, d, dtype, workspace, workspace_bytes)) != FA_OK) return s;
+  if ((s = validate_prepare(o, dO, lse, B, H, N, d, dtype, workspace, workspace_bytes)) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
-  return run_prepare(problem(B, H, N, d, 1.f, 0, nullptr, stream), dtype, o, dO, workspace);
+  return run_prepare(problem(B, H, N, d, 1.f, 0, nullptr, stream), dtype, o, dO, lse, workspace);
 }
 
 fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,

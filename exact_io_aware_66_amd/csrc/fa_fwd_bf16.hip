@@ -3,26 +3,32 @@
 // The method: tile Q, K and V into on-chip blocks; for each block of queries, walk the blocks of
 // keys/values, compute that block of scores on chip and fold it into the output with an online
 // softmax that carries a running maximum m and normaliser l per row, rescaling the partial output
-// whenever the maximum grows.  The N x N score matrix never reaches HBM, and the result is exact.
+// when the maximum grows.  The N x N score matrix never reaches HBM and the result is exact
 // (aicassindra FlashAttention architecture page, "End-to-end flow"; promptingindex page,
 // "Tiling: keeping computation inside SRAM"; NOTE-005: FlashAttention, "Method" and "Key
 // components").  The row statistic kept for the backward is LSE = m + ln l (NOTE-005, "Method").
 //
 // gfx950 design (the pages' A100 tile rule B_c = ceil(M/4d), B_r = min(B_c, d) is not used; the
-// tile is set by LDS bandwidth and register capacity of a CDNA4 compute unit):
-//   * one workgroup = 4 waves = 256 query rows of one (batch, head); each wave owns 64 rows,
-//     so every K/V byte read from LDS feeds 64 query rows (LDS traffic is half the MFMA rate);
-//   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
-//     so each lane holds one query column of the score tile and the row reductions of the
-//     softmax are in-lane plus one v_permlane32_swap;
-//   * K and V tiles of 64 keys stream through a double-buffered LDS ring with direct
-//     global->LDS 16-byte loads, prefetching tile t+1 while tile t is computed;
-//   * P^T goes from the accumulator registers straight into the B operand of O^T += V^T P^T
-//     (the key order inside each 16-key MFMA step is permuted consistently on both operands);
-//     V^T comes from LDS through the transposing read ds_read_b64_tr_b16;
-//   * the softmax works in base 2 with scale*log2(e) folded into one FMA before v_exp_f32, and
-//     normalisation by l is deferred to the epilogue;
-//   * causal: query blocks are launched heaviest first; a wave skips key tiles past its diagonal.
+// tile is set by the register file, LDS and issue model of a CDNA4 compute unit):
+//   * one workgroup = 4 waves = 256 query rows of one (batch, head), one wave per SIMD; a wave owns
+//     64 rows, so every K/V byte read from LDS feeds 64 query rows;
+//   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16);
+//     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
+//     lane halves hold different keys of the same queries and are combined once, at the end);
+//   * K and V tiles of 64 keys stream through two double-buffered LDS rings with direct
+//     global->LDS 16-byte loads; K runs one tile ahead of V, so each load has a full iteration to
+//     land before it is read;
+//   * software pipeline: S(t+1) = K(t+1) Q^T is issued on the matrix cores while the VALU turns
+//     S(t) into P(t) (exp2, bf16 pack, row sums), the two instruction streams interleaved by
+//     sched_group_barrier; then O^T += V(t)^T P(t)^T, with V^T read through ds_read_b64_tr_b16;
+//   * lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by more
+//     than 2^8 (base 2), so p <= 2^8 and the output/normaliser, which share the stale maximum, stay
+//     exact; the O rescale (128 accumulator registers) therefore runs a few times per row instead of
+//     once per tile.  Normalisation by l is deferred to the epilogue;
+//   * masked tiles (causal diagonal, key padding, ragged tail) take a separate exact path;
+//   * workgroups are ordered heaviest first (causal) and, when B*H is a multiple of 8, all query
+//     blocks of one head go to one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so a
+//     head's K/V stays in that XCD's L2.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -33,31 +39,52 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdRowsPerWave = 64;
 constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 256 query rows per workgroup
 constexpr int kFwdBc = 64;                           // keys per tile
+constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool NEG>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
-                                                          const int32_t* __restrict__ seqlens, int num_qblocks) {
-  constexpr int CH = D / 8;                   // 16-byte chunks per row
-  constexpr int TILE = kFwdBc * D * 2;        // bytes of one K or V tile
-  constexpr int LOADS = kFwdBc * CH / 256;    // 16-byte loads per thread per tile
-  constexpr int DS = D / 16;                  // k-steps of S = K Q^T
-  constexpr int DT = D / 32;                  // 32-wide d tiles of O^T
-  // Two separate LDS arrays (not one indexed ring) so the compiler can see that the prefetch into
-  // one buffer never aliases the reads of the other and does not wait for it.
-  __shared__ __attribute__((aligned(1024))) char buf0_raw[2 * TILE];  // K | V
-  __shared__ __attribute__((aligned(1024))) char buf1_raw[2 * TILE];
-  FA_LDS char* buf0 = (FA_LDS char*)buf0_raw;
-  FA_LDS char* buf1 = (FA_LDS char*)buf1_raw;
+                                                          const int32_t* __restrict__ seqlens, int nqb, int BH) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = kFwdBc * D * 2;      // bytes of one K or V tile
+  constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int DS = D / 16;                // k-steps of S = K Q^T
+  constexpr int DT = D / 32;                // 32-wide d tiles of O^T
+  constexpr bool QLDS = D == 128;           // Q fragments from LDS instead of registers
+  constexpr int VALU3 = 8 * 24;             // VALU instructions of P(t): 8 groups x (8 fma, 8 exp, 4 cvt, 4 dot)
+  // Separate LDS arrays, each referenced statically, so the compiler sees that a direct load into
+  // one buffer never aliases the reads of another.
+  __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf_raw[QLDS ? kFwdWaves * kFwdRowsPerWave * D * 2 : 16];
+  FA_LDS char* kbuf0 = (FA_LDS char*)kbuf0_raw;
+  FA_LDS char* kbuf1 = (FA_LDS char*)kbuf1_raw;
+  FA_LDS char* vbuf0 = (FA_LDS char*)vbuf0_raw;
+  FA_LDS char* vbuf1 = (FA_LDS char*)vbuf1_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int qblock = CAUSAL ? (num_qblocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t row0 = ((int64_t)b * H + h) * N;
+
+  // ---- work item: (query block, batch*head), heaviest first, XCD-local heads
+  const int wid = blockIdx.x;
+  int rank, bh;
+  if ((BH & 7) == 0) {
+    const int hpx = BH >> 3;
+    const int j = wid >> 3;
+    rank = j / hpx;
+    bh = (wid & 7) + 8 * (j - rank * hpx);
+  } else {
+    rank = wid / BH;
+    bh = wid - rank * BH;
+  }
+  const int qblock = CAUSAL ? (nqb - 1 - rank) : rank;
+  const int b = bh / H;
+  const int64_t row0 = (int64_t)bh * N;
   const __bf16* Qh = Q + row0 * D;
   const __bf16* Kh = K + row0 * D;
   const __bf16* Vh = V + row0 * D;
@@ -65,25 +92,39 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   const int L = PADDED ? clamp_len(seqlens, b, N) : N;  // keys >= L are invisible
   const int q0 = qblock * kFwdBr;
   const int qw = q0 + wave * kFwdRowsPerWave;
-  int kv_end = L;
-  if (CAUSAL) kv_end = min(kv_end, q0 + kFwdBr);
-  const int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;
-  int wave_end = kv_end;
-  if (CAUSAL) wave_end = min(kv_end, qw + kFwdRowsPerWave);
-  const int wave_tiles = wave_end > 0 ? (wave_end + kFwdBc - 1) / kFwdBc : 0;
+  const int kv_end = CAUSAL ? min(L, q0 + kFwdBr) : L;
+  const int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;  // tiles the workgroup loads
+  const int wave_end = CAUSAL ? min(L, qw + kFwdRowsPerWave) : L;
+  const int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes
+  int n_full = L / kFwdBc;                              // leading tiles with no hidden pair
+  if (CAUSAL) n_full = min(n_full, qw / kFwdBc);
 
-  // Q^T fragments (B operand): lane holds query qw + 32 qt + l32, d = 16 ds + 8 half .. +7.
-  bf16x8 qf[2][DS];
+  // Q^T fragments (B operand of S^T = K Q^T): lane holds query qw + 32 qt + l32, d = 16 ds + 8 half
+  // .. +7.  d=64: kept in registers.  d=128: the wave's 64 rows are staged once in its own LDS
+  // region (16 KiB) and the fragments are read per k-step, which keeps the wave within 256 VGPRs.
+  bf16x8 qf[2][QLDS ? 1 : DS];
+  FA_LDS char* qbuf = (FA_LDS char*)qbuf_raw + wave * (QLDS ? kFwdRowsPerWave * D * 2 : 0);
+  if constexpr (QLDS) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int row = qw + 32 * qt + l32;
+    for (int n = 0; n < kFwdRowsPerWave * CH / 64; ++n) {
+      const int p = n * 64 + lane;
+      const int r = p / CH;
+      const int c = (p % CH) ^ swz(r);
+      const int row = min(qw + r, N - 1);
+      gload_lds16(Qh + (int64_t)row * D + 8 * c, qbuf + n * 1024);
+    }
+  } else {
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      if (row < N) {
-        qf[qt][ds] = *(const bf16x8*)(Qh + (int64_t)row * D + 16 * ds + 8 * half);
-      } else {
+    for (int qt = 0; qt < 2; ++qt) {
+      const int row = qw + 32 * qt + l32;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qt][ds][e] = (__bf16)0.f;
+      for (int ds = 0; ds < DS; ++ds) {
+        if (row < N) {
+          qf[qt][ds] = *(const bf16x8*)(Qh + (int64_t)row * D + 16 * ds + 8 * half);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qt][ds][e] = (__bf16)0.f;
+        }
       }
     }
   }
@@ -93,11 +134,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = zero16();
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};  // base-2, scaled units; identical in both lane halves
+  float l_run[2] = {0.f, 0.f};              // per-lane partial normaliser (this lane's keys)
 
-  auto issue_tile = [&](int t, FA_LDS char* kdst) {
-    FA_LDS char* vdst = kdst + TILE;
+  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const int slot = (n * kFwdWaves + wave) * 64;  // first 16-byte slot of this wave's 1 KiB
@@ -105,147 +145,213 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
       const int r = p / CH;
       const int c = (p % CH) ^ swz(r);
       const int key = min(t * kFwdBc + r, N - 1);  // rows past N are masked; read a valid row
-      gload_lds16(Kh + (int64_t)key * D + 8 * c, kdst + slot * 16);
-      gload_lds16(Vh + (int64_t)key * D + 8 * c, vdst + slot * 16);
+      gload_lds16(src + (int64_t)key * D + 8 * c, dst + slot * 16);
     }
   };
 
-  // One step: wait for tile t in `cur`, start tile t+1 into `nxt`, then compute tile t.
-  auto step = [&](int t, const FA_LDS char* cur, FA_LDS char* nxt) {
+  // S^T(tile in kb) = K Q^T, 4 independent accumulators, one K fragment per (ds, kt)
+  auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[2][2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = zero16();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      bf16x8 qd[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        qd[qt] = QLDS ? lds_read_b128(qbuf, tile_off<D>(32 * qt + l32, 16 * ds + 8 * half)) : qf[qt][QLDS ? 0 : ds];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kf = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma32x32x16(kf, qd[qt], s[kt][qt]);
+      }
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {  // keep fragment reads one k-step ahead of their MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, QLDS ? 4 : 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    }
+  };
+
+  f32x16 s[2][2];  // S^T(t): s[kt][qt], lane = query column, rows = keys 32 kt + 8 (r/4) + 4 half + r%4
+  bf16x8 pf[2][4], pn[2][4];  // P(t-1) (consumed by O += P V) and P(t) (being produced), packed bf16
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  const int g = lane >> 4, j = lane & 15;
+  const int vrow = 4 * (g >> 1) + (j >> 2);
+
+  // P(t) = exp2(s cf - m) packed to bf16 (the B operand of O^T += V^T P^T), with the row sums taken
+  // by v_dot2_f32_bf16 on the packed values, so the normaliser sums exactly the weights used.
+  auto probs = [&](float cf, const float (&m_use)[2]) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kt = ks >> 1, base = 8 * (ks & 1);
+        bf16x2 pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 two = {fast_exp2(fmaf(s[kt][qt][base + 2 * e], cf, -m_use[qt])),
+                             fast_exp2(fmaf(s[kt][qt][base + 2 * e + 1], cf, -m_use[qt]))};
+          pk[e] = __builtin_convertvector(two, bf16x2);
+          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pk[e], ones, l_run[qt], false);
+        }
+        pn[qt][ks] = cat(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3));
+      }
+  };
+
+  // O^T += V^T P^T for the tile in vb, over 4 k-steps of 16 keys.  V^T fragment for (dt, ks): lane
+  // (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and 16 ks + 8 + 4 half + 0..3, the key
+  // order of pf; two transposing reads supply them.  Rows 16 ks + r and 16 ks + 8 + r share the
+  // swizzle, so every read of a lane is one base address plus a compile-time offset.
+  auto pv = [&](const FA_LDS char* vb) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t off = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 vf = cat(lds_read_tr(vb, off + ks * 16 * D * 2), lds_read_tr(vb, off + (ks * 16 + 8) * D * 2));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) acc[qt][dt] = mfma32x32x16(vf, pf[qt][ks], acc[qt][dt]);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(Kh, 0, kbuf0);
+    if (ntiles > 1) load_tile(Kh, 1, kbuf1);
+  }
+  // The first iteration adds P(-1) V(-1) with P(-1) = 0 from a zeroed buffer: an exact no-op that
+  // keeps a single (interleaved) code path for every iteration.
+  for (int i = threadIdx.x; i < TILE / 16; i += 256) *(FA_LDS u32x4*)(vbuf1 + 16 * i) = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[qt][ks][e] = (__bf16)0.f;
+  wait_vmem();
+  __syncthreads();
+  if (n_wave > 0) scores(kbuf0, s);
+
+  // Iteration t (0 <= t <= ntiles): S(t) is in s and P(t-1) in pf.  kn holds K(t+1), vp holds V(t-1);
+  // K(t+2) is loaded into kl and V(t) into vl (both last read in iteration t-1).
+  //   prepare(t) -> [ O += P(t-1) V(t-1)  ||  P(t) = exp2(...) ] -> rescale O -> S(t+1) = K(t+1) Q^T
+  auto step = [&](int t, const FA_LDS char* kn, FA_LDS char* kl, const FA_LDS char* vp, FA_LDS char* vl) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
-    if (t < wave_tiles) {
-      const FA_LDS char* kb = cur;
-      const FA_LDS char* vb = cur + TILE;
-      // ---- S^T = K Q^T for 64 keys x 64 queries: s[kt][qt]
-      f32x16 s[2][2];
+    if (t + 2 < ntiles) load_tile(Kh, t + 2, kl);
+    if (t < ntiles) load_tile(Vh, t, vl);
+    if (t > n_wave) return;  // wave-uniform: this wave has no tile left
+    const bool do_s = t < n_wave;  // else only O += P(t-1) V(t-1) remains; P(t) is forced to 0
+
+    // ---- prepare: the lazy maximum check (fully visible tile) or mask + exact update
+    // Defaults are for the drain iteration (no P(t)): exp2(s * 1 - inf) = 0 for every s this wave can
+    // hold (finite raw scores, or the -inf of hidden pairs), so nothing is added to l.
+    float cf = 1.f, m_use[2] = {INFINITY, INFINITY}, alpha[2] = {1.f, 1.f};
+    bool raise = false;
+    if (do_s) {
+      if (t < n_full) {
+        float tm[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int qt = 0; qt < 2; ++qt) {
+          float e = s[0][qt][0];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = zero16();
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 kf = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma32x32x16(kf, qf[qt][ds], s[kt][qt]);
+            for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) e = NEG ? fminf(e, s[kt][qt][r]) : fmaxf(e, s[kt][qt][r]);
+          e = NEG ? min_halves(e) : max_halves(e);
+          tm[qt] = e * c_log2;
         }
-      }
-      // ---- mask (only tiles that reach past L or the wave's diagonal).  A masked tile is moved to
-      // the scaled domain t = s * scale * log2(e) first, with -inf for hidden pairs, so the update
-      // below runs with a unit factor (a hidden pair never meets a zero or negative scale).
-      const int key0 = t * kFwdBc;
-      const bool need_mask = (key0 + kFwdBc > L) || (CAUSAL && key0 + kFwdBc - 1 > qw);
-      float cf = c_log2;
-      if (need_mask) {
-        cf = 1.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        raise = __any((tm[0] > m_run[0] + kLazyRescale) || (tm[1] > m_run[1] + kLazyRescale));
+        if (raise) {
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
-            const int query = qw + 32 * qt + l32;
+            const float m_new = fmaxf(m_run[qt], tm[qt]);
+            alpha[qt] = fast_exp2(m_run[qt] - m_new);
+            m_run[qt] = m_new;
+          }
+        }
+        cf = c_log2;
+        m_use[0] = m_run[0];
+        m_use[1] = m_run[1];
+      } else {
+        const int key0 = t * kFwdBc;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int query = qw + 32 * qt + l32;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
               const bool vis = key < L && (!CAUSAL || key <= query);
-              s[kt][qt][r] = vis ? s[kt][qt][r] * c_log2 : -INFINITY;
+              const float v = vis ? s[kt][qt][r] * c_log2 : -INFINITY;
+              s[kt][qt][r] = v;
+              mx = fmaxf(mx, v);
             }
-          }
-      }
-      // ---- online softmax (base 2): m, l per query column; rescale O^T columns by alpha
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float ext;
-        if (cf >= 0.f) {
-          float mx = s[0][qt][0];
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
-          ext = max_halves(mx);
-        } else {
-          float mn = s[0][qt][0];
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mn = fminf(mn, s[kt][qt][r]);
-          ext = min_halves(mn);
+          mx = max_halves(mx);
+          const float m_new = fmaxf(m_run[qt], mx);
+          m_use[qt] = (m_new == -INFINITY) ? 0.f : m_new;
+          alpha[qt] = fast_exp2(m_run[qt] - m_use[qt]);
+          m_run[qt] = m_new;
         }
-        const float tile_max = (ext == -INFINITY) ? -INFINITY : ext * cf;
-        const float m_new = fmaxf(m_run[qt], tile_max);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qt] - m_use);
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[kt][qt][r], cf, -m_use));
-            s[kt][qt][r] = p;
-            rs += p;
-          }
-        rs = add_halves(rs);
-        l_run[qt] = l_run[qt] * alpha + rs;
-        m_run[qt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
+        cf = 1.f;
+        raise = __any(alpha[0] != 1.f || alpha[1] != 1.f);
       }
-      // ---- O^T += V^T P^T over 4 k-steps of 16 keys
-      bf16x8 pf[2][4];
+      l_run[0] *= alpha[0];
+      l_run[1] *= alpha[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- O += P(t-1) V(t-1) on the matrix cores, interleaved with P(t) on the VALU
+    probs(cf, m_use);
+    pv(vp);
+#pragma unroll
+    for (int i = 0; i < 8 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, VALU3 / (8 * DT), 0);
+    }
+    // Pin P(t) and the row sums here: without a use inside this phase the compiler sinks their
+    // computation past the matrix-core work it is meant to overlap.
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(pn[qt][ks]));
+    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    if (raise) {  // O carries P(t-1) at the old maximum: scale it to the new one
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pack8(s[ks >> 1][qt], 8 * (ks & 1));
-      // V^T fragment for (dt, ks): lane (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and
-      // 16 ks + 8 + 4 half + 0..3, the same key order as pf.  Two transposing reads supply them.
-      // Rows 16 ks + r and 16 ks + 8 + r share the swizzle, so every read of a lane is one base
-      // address plus a compile-time offset.
-      const int g = lane >> 4, j = lane & 15;
-      const int vrow = 4 * (g >> 1) + (j >> 2);
-      u32x2 vfr[2][4][2];
-      auto read_v = [&](u32x2 (&dst)[4][2], int dt) {
-        const uint32_t base = lds_addr(vb) + tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
-        dst[0][0] = lds_read_tr_asm<0 * 16 * D * 2>(base);
-        dst[0][1] = lds_read_tr_asm<(0 * 16 + 8) * D * 2>(base);
-        dst[1][0] = lds_read_tr_asm<1 * 16 * D * 2>(base);
-        dst[1][1] = lds_read_tr_asm<(1 * 16 + 8) * D * 2>(base);
-        dst[2][0] = lds_read_tr_asm<2 * 16 * D * 2>(base);
-        dst[2][1] = lds_read_tr_asm<(2 * 16 + 8) * D * 2>(base);
-        dst[3][0] = lds_read_tr_asm<3 * 16 * D * 2>(base);
-        dst[3][1] = lds_read_tr_asm<(3 * 16 + 8) * D * 2>(base);
-      };
-      read_v(vfr[0], 0);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x2 (&cur)[4][2] = vfr[dt & 1];
-        lds_wait(cur[0][0], cur[0][1], cur[1][0], cur[1][1], cur[2][0], cur[2][1], cur[3][0], cur[3][1]);
-        if (dt + 1 < DT) read_v(vfr[(dt + 1) & 1], dt + 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 vf = cat(cur[ks][0], cur[ks][1]);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) acc[qt][dt] = mfma32x32x16(vf, pf[qt][ks], acc[qt][dt]);
-        }
-      }
+        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha[qt];
     }
+    // ---- S(t+1) = K(t+1) Q^T
+    if (t + 1 < n_wave) scores(kn, s);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pn[qt][ks];
   };
 
-  if (ntiles > 0) issue_tile(0, buf0);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, buf0, buf1);
-    if (t + 1 < ntiles) step(t + 1, buf1, buf0);
+  for (int t = 0; t <= ntiles; t += 2) {
+    step(t, kbuf1, kbuf0, vbuf1, vbuf0);
+    if (t + 1 <= ntiles) step(t + 1, kbuf0, kbuf1, vbuf0, vbuf1);
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int query = qw + 32 * qt + l32;
-    const bool has = l_run[qt] > 0.f;
-    const float inv = has ? 1.f / l_run[qt] : 0.f;
+    const float l = add_halves(l_run[qt]);
+    const bool has = l > 0.f;
+    const float inv = has ? 1.f / l : 0.f;
     if (query < N) {
-      if (half == 0) LSE[row0 + query] = has ? (m_run[qt] + __log2f(l_run[qt])) * kLn2 : -INFINITY;
+      if (half == 0) LSE[row0 + query] = has ? (m_run[qt] + __log2f(l)) * kLn2 : -INFINITY;
       __bf16* orow = O + (row0 + query) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -260,24 +366,33 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool NEG>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const int nqb = (p.N + kFwdBr - 1) / kFwdBr;
-  dim3 grid(nqb, p.H, p.B);
+  const int BH = p.B * p.H;
   const float c_log2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED>), grid, dim3(256), 0, p.stream, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2, p.seqlens, nqb);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2,
+                     p.seqlens, nqb, BH);
   return hipGetLastError();
+}
+
+template <int D, bool NEG>
+hipError_t launch_mask(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
+  const bool pad = p.seqlens != nullptr;
+  if (p.causal)
+    return pad ? launch<D, true, true, NEG>(p, q, k, v, o, lse) : launch<D, true, false, NEG>(p, q, k, v, o, lse);
+  return pad ? launch<D, false, true, NEG>(p, q, k, v, o, lse) : launch<D, false, false, NEG>(p, q, k, v, o, lse);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
-  const bool pad = p.seqlens != nullptr;
-  if (p.causal) return pad ? launch<D, true, true>(p, q, k, v, o, lse) : launch<D, true, false>(p, q, k, v, o, lse);
-  return pad ? launch<D, false, true>(p, q, k, v, o, lse) : launch<D, false, false>(p, q, k, v, o, lse);
+  return p.scale < 0.f ? launch_mask<D, true>(p, q, k, v, o, lse) : launch_mask<D, false>(p, q, k, v, o, lse);
 }
 
 }  // namespace
+
+int64_t fwd_bf16_grid(int B, int H, int N) { return (int64_t)((N + kFwdBr - 1) / kFwdBr) * B * H; }
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   return p.d == 64 ? launch_d<64>(p, q, k, v, o, lse) : launch_d<128>(p, q, k, v, o, lse);

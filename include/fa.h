@@ -78,9 +78,10 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes: one float32 per row for
- * D_i = sum_c dO_ic O_ic, plus (bf16 only) a float32 [B][H][N][d] accumulator for dQ.
- * Returns 0 for invalid or unsupported sizes.  Linear in N (O(N) extra memory; NOTE-005 "Key
- * results", Theorem 1).
+ * D_i = sum_c dO_ic O_ic, plus (bf16 only) one float32 per row for LSE_i log2(e) and a float32
+ * [B][H][Npad][d] accumulator for dQ, Npad = N rounded up to a multiple of 64.  Returns 0 for
+ * invalid or unsupported sizes.  Linear in N (O(N) extra memory; NOTE-005 "Key results",
+ * Theorem 1).
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d, fa_dtype_t dtype);
 
@@ -103,8 +104,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
 /*
  * The backward in its three stages, for callers that schedule or time them separately.
  * fa_backward(...) is exactly these three calls in order on one stream, with the same workspace:
- *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; clears the dQ accumulator
- *                         (bf16).  Reads o and dO only.
+ *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; for bf16 also LSE_i log2(e)
+ *                         and a cleared dQ accumulator.  Reads o, dO and lse only.
  *   fa_backward_main    : the recompute pass over key blocks: writes dk, dv, and accumulates dQ
  *                         (bf16: into the workspace; float32: straight into dq).  Needs the
  *                         workspace as fa_backward_prepare left it.
@@ -112,8 +113,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
  *                         float32 (returns FA_OK).
  * Arguments, layout and errors as in fa_backward.
  */
-fa_status_t fa_backward_prepare(const void* o, const void* dO, int B, int H, int N, int d, fa_dtype_t dtype,
-                                void* workspace, size_t workspace_bytes, void* stream);
+fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                                fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                              int causal, const int32_t* seqlens, fa_dtype_t dtype, void* workspace,
