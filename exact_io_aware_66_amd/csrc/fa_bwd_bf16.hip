@@ -17,8 +17,10 @@
 //                tile u, one barrier, then
 //                  A: dQ(u-1) = dS(u-1) K on the matrix cores (dS^T of all four waves from LDS),
 //                     interleaved with P(u) = exp2(S scale log2 e - LSE log2 e) and
-//                     dS(u) = P (dP - D) on the VALU; dS^T(u) goes to LDS; dQ(u-1) is added to
-//                     the fp32 accumulator with float atomics (one per element per key block);
+//                     dS(u) = P (dP - D) on the VALU; dS^T(u) goes to LDS.  dQ(u-1) is added to
+//                     the fp32 accumulator with float atomics (one per element per key block) at
+//                     the start of the next iteration, next to the tile loads, so the wait for
+//                     those loads never waits for freshly issued atomics;
 //                  B: dV^T += dO^T P(u), dK^T += Q^T dS(u) (dO^T, Q^T via transposing LDS reads);
 //                  C: S(u+1) = Q K^T, dP(u+1) = dO V^T.
 //                Tiles with hidden pairs (causal diagonal, key padding, ragged tail) first set the
@@ -90,15 +92,16 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* __restric
 template <int D>
 constexpr int bwd_rows_per_tile() { return D == 128 ? 32 : 64; }
 
-// Byte offset of (key row, query col) in the dS^T tile [128 keys][BR queries] (bf16), swizzled so
-// that both the per-key 8-byte writes and the transposing reads are free of bank conflicts.  Rows
-// r, r + 8 and r + 16 share the swizzle.
+// Byte offset of (key row, query col) in the dS^T tile [128 keys][BR queries] (bf16).  BR = 64:
+// 128-byte rows with the tile swizzle.  BR = 32: 64-byte rows, four to a 256-byte bank range, so a
+// transposing read (4 consecutive rows) is conflict-free as is; the 8-byte chunk index is XORed with
+// row / 4 so that the per-key writes of 32 consecutive keys land on distinct banks.
 template <int BR>
 __device__ __forceinline__ uint32_t dst_off(int row, int col) {
   if constexpr (BR == 64) {
     return tile_off<64>(row, col);
   } else {
-    return (uint32_t)(row * (BR * 2) + (((col >> 2) ^ (row & 7)) << 3) + ((col & 3) << 1));
+    return (uint32_t)(row * (BR * 2) + (((col >> 2) ^ ((row >> 2) & 7)) << 3) + ((col & 3) << 1));
   }
 }
 
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
   FA_LDS char* kst = (FA_LDS char*)kst_raw;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -201,6 +204,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
     const int qsw = wave / DT, dtq = wave % DT;
     const int dcol = 32 * dtq + 16 * (g16 & 1) + 4 * (j16 & 3);
     const int trow = 4 * (g16 >> 1) + (j16 >> 2);
+    // per-lane LDS bases of the transposing reads of the dQ product (see the dQ phase)
+    const uint32_t kb0 = tile_off<D>(trow, dcol), kb8 = tile_off<D>(trow + 8, dcol);
+    uint32_t dsb[2][2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        dsb[par][hh] = dst_off<BR>(trow + 16 * par + 8 * hh, 32 * qsw + 16 * (g16 & 1) + 4 * (j16 & 3));
 
     const int nqt = (N + BR - 1) / BR;
     const int it0 = CAUSAL ? (k0 / BR) : 0;
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
         const int slot = (n * kBwdWaves + wave) * 64;
         const int p = slot + lane;
         const int r = p / CH;
-        const int c = (p % CH) ^ swz(r);
+        const int c = (p % CH) ^ swz<D>(r);
         const int q = min(qbase + r, N - 1);
         gload_lds16(Qh + (int64_t)q * D + 8 * c, dst + slot * 16);
         gload_lds16(dOh + (int64_t)q * D + 8 * c, dst + QTILE + slot * 16);
@@ -242,22 +253,31 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
           s[qs] = mfma32x32x16(qa, kb[ds], s[qs]);
           dp[qs] = mfma32x32x16(da, vb[ds], dp[qs]);
         }
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {  // fragment reads one k-step ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * QS, 1);
-      }
+      pipe_schedule<DS, 2 * QS, 2 * QS, 0, 2, 1>();  // fragment reads two k-steps ahead of their MFMAs
     };
 
     bf16x8 pb[2 * QS], db[2 * QS];  // P and dS packed (B operands of dV^T and dK^T), k = queries
+    f32x16 accq = zero16();          // dQ tile of the previous query tile, added one iteration later
+
+    // dQ(tile v) += accq: float atomics into the row-padded accumulator (unscaled).  Lane holds
+    // d = 32 dtq + l32 and queries 8 g + 4 half + e of the wave's 32-row half; one base per g keeps
+    // every offset an instruction immediate.
+    auto add_dq = [&](int v) {
+      float* base = dQh + (int64_t)((it0 + v) * BR + 32 * qsw + 4 * half) * D + 32 * dtq + l32;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) unsafeAtomicAdd(base + (8 * gq + e) * D, accq[4 * gq + e]);
+    };
 
     // One tile: tile u in cur (Q, dO, LSE log2 e, D); st_next holds tile u+1; tile u+2 is loaded
     // into st_load.  dsw receives dS^T(u); dsr holds dS^T(u-1).
     auto step = [&](int u, const FA_LDS char* cur, const FA_LDS char* st_next, FA_LDS char* st_load,
                     FA_LDS char* dsw, const FA_LDS char* dsr) {
-      wait_vmem();
+      wait_vmem();  // tile u+1 landed; the atomics issued one iteration ago have completed
       __syncthreads();
       if (u + 2 < count) load_tile(u + 2, st_load);
+      if (u >= 2) add_dq(u - 2);  // issued now so that they too have a full iteration to complete
       const int qi0 = (it0 + u) * BR;
       const bool has = u < count;
 
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int query = qi0 + 32 * qs + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = my_key < L && query < N && (!CAUSAL || my_key <= query);
+            const bool vis = (my_key < L) & (query < N) & (!CAUSAL | (my_key <= query));
             s[qs][r] = vis ? s[qs][r] * c_log2 : -INFINITY;
           }
         cf = 1.f;
@@ -299,23 +319,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
         pb[ks] = pack8(s[ks >> 1], 8 * (ks & 1));
         db[ks] = pack8(dp[ks >> 1], 8 * (ks & 1));
       }
-      f32x16 accq = zero16();
-      {
-        const uint32_t sbase = dst_off<BR>(trow, 32 * qsw + 16 * (g16 & 1) + 4 * (j16 & 3));
-        const uint32_t kbase = tile_off<D>(trow, dcol);
+      accq = zero16();
 #pragma unroll
-        for (int ks = 0; ks < kBwdBc / 16; ++ks) {
-          const bf16x8 sa = cat(lds_read_tr(dsr, sbase + ks * 16 * BR * 2), lds_read_tr(dsr, sbase + (ks * 16 + 8) * BR * 2));
-          const bf16x8 kq = cat(lds_read_tr(kst, kbase + ks * 16 * D * 2), lds_read_tr(kst, kbase + (ks * 16 + 8) * D * 2));
-          accq = mfma32x32x16(sa, kq, accq);
-        }
+      for (int ks = 0; ks < kBwdBc / 16; ++ks) {
+        // dS^T rows trow + 16 ks and trow + 16 ks + 8 (per-lane bases for the parity of ks and the
+        // +8: the swizzles repeat every 32 rows of dS^T and 16 rows of K)
+        const uint32_t srow = dsb[ks & 1][0] + (ks >> 1) * 32 * BR * 2;
+        const uint32_t srow8 = dsb[ks & 1][1] + (ks >> 1) * 32 * BR * 2;
+        const bf16x8 sa = cat(lds_read_tr(dsr, srow), lds_read_tr(dsr, srow8));
+        const bf16x8 kq = cat(lds_read_tr(kst, kb0 + ks * 16 * D * 2), lds_read_tr(kst, kb8 + ks * 16 * D * 2));
+        accq = mfma32x32x16(sa, kq, accq);
       }
-#pragma unroll
-      for (int i = 0; i < kBwdBc / 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads (next MFMA's operands)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, VALU_A / (kBwdBc / 16), 0);
-      }
+      pipe_schedule<kBwdBc / 16, 4, 1, VALU_A / (kBwdBc / 16), 2, 0>();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 2 * QS; ++ks) asm volatile("" : "+v"(pb[ks]), "+v"(db[ks]));
@@ -327,34 +342,22 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
         *(FA_LDS bf16x4*)(dsw + dst_off<BR>(32 * wave + l32, qloc)) = __builtin_shufflevector(db[ks], db[ks], 0, 1, 2, 3);
         *(FA_LDS bf16x4*)(dsw + dst_off<BR>(32 * wave + l32, qloc + 8)) = __builtin_shufflevector(db[ks], db[ks], 4, 5, 6, 7);
       }
-      // dQ(u-1) += dS(u-1) K: float atomics into the row-padded accumulator (unscaled)
-      if (u >= 1) {
-        const int qp0 = qi0 - BR + 32 * qsw;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = qp0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          unsafeAtomicAdd(dQh + (int64_t)query * D + 32 * dtq + l32, accq[r]);
-        }
-      }
       if (!has) return;
 
       // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t tb = tile_off<D>(trow, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3));
+        const uint32_t tb0 = tile_off<D>(trow, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3));
+        const uint32_t tb8 = tile_off<D>(trow + 8, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3));
 #pragma unroll
         for (int ks = 0; ks < 2 * QS; ++ks) {
-          const bf16x8 da = cat(lds_read_tr(cur + QTILE, tb + ks * 16 * D * 2), lds_read_tr(cur + QTILE, tb + (ks * 16 + 8) * D * 2));
-          const bf16x8 qa = cat(lds_read_tr(cur, tb + ks * 16 * D * 2), lds_read_tr(cur, tb + (ks * 16 + 8) * D * 2));
+          const bf16x8 da = cat(lds_read_tr(cur + QTILE, tb0 + ks * 16 * D * 2), lds_read_tr(cur + QTILE, tb8 + ks * 16 * D * 2));
+          const bf16x8 qa = cat(lds_read_tr(cur, tb0 + ks * 16 * D * 2), lds_read_tr(cur, tb8 + ks * 16 * D * 2));
           dvt[dt] = mfma32x32x16(da, pb[ks], dvt[dt]);
           dkt[dt] = mfma32x32x16(qa, db[ks], dkt[dt]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 2 * QS * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
-      }
+      pipe_schedule<2 * QS * DT, 4, 2, 0, 2, 2>();
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- C: S(u+1), dP(u+1)
@@ -371,6 +374,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const __bf16* __restri
       if (u + 1 <= count) step(u + 1, st1, st2, st0, ds1, ds0);
       if (u + 2 <= count) step(u + 2, st2, st0, st1, ds2, ds1);
     }
+    add_dq(count - 1);  // dQ of the last tile, computed in the drain iteration
   }
 
   // ---- dK = scale dS^T Q, dV: lane holds key my_key, d = 32 dt + 8 g + 4 half + 0..3

@@ -44,17 +44,43 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// XOR swizzle of the 16-byte chunk index inside one LDS row, keyed by the row.  Any 8 consecutive
-// rows read at the same logical chunk land on 8 different chunk positions (conflict-free 128-bit
-// reads), and any 4 consecutive rows starting at a multiple of 4 keep each aligned pair of chunks
-// together while moving the pairs apart (conflict-free transposing 64-bit reads).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzle of the 16-byte chunk index inside one row of a row-major bf16 LDS tile with NCOL
+// columns, keyed by the row.  gfx950's LDS serves a transposing 64-bit read 32 lanes (256 bytes, 64
+// banks) at a time; in our reads those lanes cover 4 consecutive rows (aligned to 4) x 4 aligned
+// chunks, so the 4 rows must land on disjoint bank ranges.  128-bit reads of 16 consecutive rows at
+// one logical chunk must land on distinct chunk positions too.
+//   256-byte rows (NCOL = 128): s(r) = 4 (r mod 4) + (r / 4 mod 4)
+//   128-byte rows (NCOL = 64):  s(r) = 4 (r / 2 mod 2) + (r / 4 mod 4)   (two rows share a bank range)
+// In both, s(r + 16) = s(r) and s(r + 8) = s(r) xor 2.
+template <int NCOL>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(NCOL == 64 || NCOL == 128, "swizzle defined for 128- and 256-byte rows");
+  return NCOL == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
-// Byte offset of (row, element col) in a row-major LDS tile of `ncol` bf16 per row, swizzled.
+// Byte offset of (row, element col) in a row-major LDS tile of NCOL bf16 per row, swizzled.
 template <int NCOL>
 __device__ __forceinline__ uint32_t tile_off(int row, int col) {
   const int c = col >> 3;
-  return (uint32_t)(row * (NCOL * 2) + ((c ^ swz(row)) << 4) + ((col & 7) << 1));
+  return (uint32_t)(row * (NCOL * 2) + ((c ^ swz<NCOL>(row)) << 4) + ((col & 7) << 1));
+}
+
+// Software-pipelined schedule for STEPS steps of (R LDS reads -> M MFMAs [+ V VALU]): the reads
+// run AHEAD steps in front of the MFMAs that consume them, so LDS latency overlaps matrix work.
+// Applies to the instructions of the current scheduling region (sync id SYNC).
+template <int STEPS, int R, int M, int V, int AHEAD, int SYNC>
+__device__ __forceinline__ void pipe_schedule() {
+#pragma unroll
+  for (int i = 0; i < AHEAD && i < STEPS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, R, SYNC);
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
+      if (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, SYNC);
+    }
+    if (i + AHEAD < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, R, SYNC);
+  }
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const FA_LDS char* base, uint32_t off) {

@@ -36,13 +36,16 @@ namespace fa {
 namespace {
 
 constexpr int kFwdWaves = 4;
-constexpr int kFwdRowsPerWave = 64;
-constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 256 query rows per workgroup
+// Query rows per wave.  32: a wave fits in 256 registers and two workgroups share a compute unit,
+// each covering the other's memory and barrier stalls.  64: one workgroup per compute unit, and
+// every K/V fragment read from LDS feeds twice as many rows.
+constexpr int kFwdRowsPerWave = FA_FWD_ROWS_PER_WAVE;
+constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // query rows per workgroup
 constexpr int kFwdBc = 64;                           // keys per tile
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
 template <int D, bool CAUSAL, bool PADDED, bool NEG>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens, int nqb, int BH) {
@@ -51,8 +54,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
   constexpr int DS = D / 16;                // k-steps of S = K Q^T
   constexpr int DT = D / 32;                // 32-wide d tiles of O^T
-  constexpr bool QLDS = D == 128;           // Q fragments from LDS instead of registers
-  constexpr int VALU3 = 8 * 24;             // VALU instructions of P(t): 8 groups x (8 fma, 8 exp, 4 cvt, 4 dot)
+  constexpr int QT = kFwdRowsPerWave / 32;  // 32-row query halves of a wave
+  constexpr bool QLDS = D == 128 && QT == 2;  // Q fragments from LDS instead of registers
+  constexpr int VALU3 = QT * 4 * 24;        // VALU instructions of P(t): 4 QT groups x (8 fma, 8 exp, 4 cvt, 4 dot)
   // Separate LDS arrays, each referenced statically, so the compiler sees that a direct load into
   // one buffer never aliases the reads of another.
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   FA_LDS char* vbuf1 = (FA_LDS char*)vbuf1_raw;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -102,20 +106,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   // Q^T fragments (B operand of S^T = K Q^T): lane holds query qw + 32 qt + l32, d = 16 ds + 8 half
   // .. +7.  d=64: kept in registers.  d=128: the wave's 64 rows are staged once in its own LDS
   // region (16 KiB) and the fragments are read per k-step, which keeps the wave within 256 VGPRs.
-  bf16x8 qf[2][QLDS ? 1 : DS];
+  bf16x8 qf[QT][QLDS ? 1 : DS];
   FA_LDS char* qbuf = (FA_LDS char*)qbuf_raw + wave * (QLDS ? kFwdRowsPerWave * D * 2 : 0);
   if constexpr (QLDS) {
 #pragma unroll
     for (int n = 0; n < kFwdRowsPerWave * CH / 64; ++n) {
       const int p = n * 64 + lane;
       const int r = p / CH;
-      const int c = (p % CH) ^ swz(r);
+      const int c = (p % CH) ^ swz<D>(r);
       const int row = min(qw + r, N - 1);
       gload_lds16(Qh + (int64_t)row * D + 8 * c, qbuf + n * 1024);
     }
   } else {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const int row = qw + 32 * qt + l32;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
@@ -129,13 +133,17 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
     }
   }
 
-  f32x16 acc[2][DT];
+  f32x16 acc[QT][DT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = zero16();
-  float m_run[2] = {-INFINITY, -INFINITY};  // base-2, scaled units; identical in both lane halves
-  float l_run[2] = {0.f, 0.f};              // per-lane partial normaliser (this lane's keys)
+  float m_run[QT], l_run[QT];  // base-2 running maximum (identical in both lane halves); per-lane
+#pragma unroll                 // partial normaliser (this lane's keys)
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
 
   auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
 #pragma unroll
@@ -143,49 +151,45 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
       const int slot = (n * kFwdWaves + wave) * 64;  // first 16-byte slot of this wave's 1 KiB
       const int p = slot + lane;
       const int r = p / CH;
-      const int c = (p % CH) ^ swz(r);
+      const int c = (p % CH) ^ swz<D>(r);
       const int key = min(t * kFwdBc + r, N - 1);  // rows past N are masked; read a valid row
       gload_lds16(src + (int64_t)key * D + 8 * c, dst + slot * 16);
     }
   };
 
   // S^T(tile in kb) = K Q^T, 4 independent accumulators, one K fragment per (ds, kt)
-  auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[2][2]) {
+  auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[2][QT]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = zero16();
+      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = zero16();
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      bf16x8 qd[2];
+      bf16x8 qd[QT];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
         qd[qt] = QLDS ? lds_read_b128(qbuf, tile_off<D>(32 * qt + l32, 16 * ds + 8 * half)) : qf[qt][QLDS ? 0 : ds];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 kf = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma32x32x16(kf, qd[qt], s[kt][qt]);
+        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma32x32x16(kf, qd[qt], s[kt][qt]);
       }
     }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {  // keep fragment reads one k-step ahead of their MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, QLDS ? 4 : 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-    }
+    pipe_schedule<DS, QLDS ? 4 : 2, 2 * QT, 0, 2, 1>();  // fragment reads two k-steps ahead of their MFMAs
   };
 
-  f32x16 s[2][2];  // S^T(t): s[kt][qt], lane = query column, rows = keys 32 kt + 8 (r/4) + 4 half + r%4
-  bf16x8 pf[2][4], pn[2][4];  // P(t-1) (consumed by O += P V) and P(t) (being produced), packed bf16
+  f32x16 s[2][QT];  // S^T(t): s[kt][qt], lane = query column, rows = keys 32 kt + 8 (r/4) + 4 half + r%4
+  bf16x8 pf[QT][4], pn[QT][4];  // P(t-1) (consumed by O += P V) and P(t) (being produced), packed bf16
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   const int g = lane >> 4, j = lane & 15;
   const int vrow = 4 * (g >> 1) + (j >> 2);
 
   // P(t) = exp2(s cf - m) packed to bf16 (the B operand of O^T += V^T P^T), with the row sums taken
   // by v_dot2_f32_bf16 on the packed values, so the normaliser sums exactly the weights used.
-  auto probs = [&](float cf, const float (&m_use)[2]) {
+  auto probs = [&](float cf, const float (&m_use)[QT]) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kt = ks >> 1, base = 8 * (ks & 1);
@@ -204,17 +208,19 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
 
   // O^T += V^T P^T for the tile in vb, over 4 k-steps of 16 keys.  V^T fragment for (dt, ks): lane
   // (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and 16 ks + 8 + 4 half + 0..3, the key
-  // order of pf; two transposing reads supply them.  Rows 16 ks + r and 16 ks + 8 + r share the
-  // swizzle, so every read of a lane is one base address plus a compile-time offset.
+  // order of pf; two transposing reads supply them.  Each lane reads from two base addresses (rows
+  // vrow and vrow + 8) plus compile-time offsets of 16 rows.
   auto pv = [&](const FA_LDS char* vb) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t off = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
+      // rows vrow + 16 ks share the swizzle; rows vrow + 8 + 16 ks need their own base
+      const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
+      const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 vf = cat(lds_read_tr(vb, off + ks * 16 * D * 2), lds_read_tr(vb, off + (ks * 16 + 8) * D * 2));
+        const bf16x8 vf = cat(lds_read_tr(vb, off0 + ks * 16 * D * 2), lds_read_tr(vb, off8 + ks * 16 * D * 2));
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) acc[qt][dt] = mfma32x32x16(vf, pf[qt][ks], acc[qt][dt]);
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32x32x16(vf, pf[qt][ks], acc[qt][dt]);
       }
     }
   };
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
   // keeps a single (interleaved) code path for every iteration.
   for (int i = threadIdx.x; i < TILE / 16; i += 256) *(FA_LDS u32x4*)(vbuf1 + 16 * i) = u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -250,13 +256,18 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
     // ---- prepare: the lazy maximum check (fully visible tile) or mask + exact update
     // Defaults are for the drain iteration (no P(t)): exp2(s * 1 - inf) = 0 for every s this wave can
     // hold (finite raw scores, or the -inf of hidden pairs), so nothing is added to l.
-    float cf = 1.f, m_use[2] = {INFINITY, INFINITY}, alpha[2] = {1.f, 1.f};
+    float cf = 1.f, m_use[QT], alpha[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      m_use[qt] = INFINITY;
+      alpha[qt] = 1.f;
+    }
     bool raise = false;
     if (do_s) {
       if (t < n_full) {
-        float tm[2];
+        float tm[QT];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
           float e = s[0][qt][0];
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
@@ -265,22 +276,25 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
           e = NEG ? min_halves(e) : max_halves(e);
           tm[qt] = e * c_log2;
         }
-        raise = __any((tm[0] > m_run[0] + kLazyRescale) || (tm[1] > m_run[1] + kLazyRescale));
+        bool over = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) over |= tm[qt] > m_run[qt] + kLazyRescale;
+        raise = __builtin_amdgcn_readfirstlane(__any(over));
         if (raise) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
+          for (int qt = 0; qt < QT; ++qt) {
             const float m_new = fmaxf(m_run[qt], tm[qt]);
             alpha[qt] = fast_exp2(m_run[qt] - m_new);
             m_run[qt] = m_new;
           }
         }
         cf = c_log2;
-        m_use[0] = m_run[0];
-        m_use[1] = m_run[1];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) m_use[qt] = m_run[qt];
       } else {
         const int key0 = t * kFwdBc;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
           const int query = qw + 32 * qt + l32;
           float mx = -INFINITY;
 #pragma unroll
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-              const bool vis = key < L && (!CAUSAL || key <= query);
+              const bool vis = (key < L) & (!CAUSAL | (key <= query));
               const float v = vis ? s[kt][qt][r] * c_log2 : -INFINITY;
               s[kt][qt][r] = v;
               mx = fmaxf(mx, v);
@@ -300,40 +314,40 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
           m_run[qt] = m_new;
         }
         cf = 1.f;
-        raise = __any(alpha[0] != 1.f || alpha[1] != 1.f);
+        bool changed = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) changed |= alpha[qt] != 1.f;
+        raise = __builtin_amdgcn_readfirstlane(__any(changed));
       }
-      l_run[0] *= alpha[0];
-      l_run[1] *= alpha[1];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) l_run[qt] *= alpha[qt];
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O += P(t-1) V(t-1) on the matrix cores, interleaved with P(t) on the VALU
     probs(cf, m_use);
     pv(vp);
-#pragma unroll
-    for (int i = 0; i < 8 * DT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, VALU3 / (8 * DT), 0);
-    }
+    // 4 DT steps of (2 transposing reads -> 2 MFMAs), each MFMA followed by its share of the VALU work
+    pipe_schedule<4 * DT, 2, QT, VALU3 / (4 * DT * QT), 2, 0>();
     // Pin P(t) and the row sums here: without a use inside this phase the compiler sinks their
     // computation past the matrix-core work it is meant to overlap.
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(pn[qt][ks]));
-    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(l_run[qt]));
     __builtin_amdgcn_sched_barrier(0);
     if (raise) {  // O carries P(t-1) at the old maximum: scale it to the new one
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha[qt];
     }
     // ---- S(t+1) = K(t+1) Q^T
     if (t + 1 < n_wave) scores(kn, s);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pn[qt][ks];
   };
@@ -345,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const __bf16* __restri
 
   // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int query = qw + 32 * qt + l32;
     const float l = add_halves(l_run[qt]);
     const bool has = l > 0.f;
