@@ -2,14 +2,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
 
-One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_main,
-fa_backward_finish -- exactly what fa_backward runs) over one batch of the synthetic workload,
+One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_dkdv,
+fa_backward_dq -- exactly what fa_backward runs) over one batch of the synthetic workload,
 inputs resident in HBM.  W untimed steps, then K timed steps bracketed by synchronisation and
 HIP events on the stream the kernels run on; per-stage HIP events inside the timed region give the
 average duration of each kernel launch.
 
 FLOPs are algorithmic: forward 4 d per visible (query, key) pair (QK^T and PV), backward 2.5x
-forward (QK^T recomputed, dO V^T, P^T dO, dS^T Q, dS K).  Causal pairs per head N(N+1)/2.
+forward (QK^T recomputed, dO V^T, P^T dO, dS^T Q, dS K), of which the dK/dV pass is credited with
+the first four products (8 d per pair) and the dQ pass with dS K (2 d per pair; it recomputes
+QK^T and dO V^T as well, which counts as overhead, not as work).  Causal pairs per head N(N+1)/2.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -40,7 +42,7 @@ def workload_flops(w, x):
     lens = [w.N] * w.B if x["seqlens"] is None else [int(s) for s in x["seqlens"]]
     pairs = sum(visible_pairs(w.N, w.causal, L) for L in lens) * w.H
     fwd = 4.0 * w.d * pairs
-    return fwd, 2.5 * fwd
+    return fwd, 2.5 * fwd, 2.0 * fwd, 0.5 * fwd
 
 
 def cpu_baseline(w, x, target_s: float = 12.0):
@@ -113,7 +115,7 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
     scale, causal = x["scale"], w.causal
-    flops_fwd, flops_bwd = workload_flops(w, x)
+    flops_fwd, flops_bwd, flops_dkdv, flops_dq = workload_flops(w, x)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -124,9 +126,9 @@ def main():
         if e: e[1].record(stream)
         fa.fa_backward_prepare(o, do, lse, ws)
         if e: e[2].record(stream)
-        fa.fa_backward_main(q, k, v, do, lse, dq, dk, dv, scale, causal, sl, ws)
+        fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale, causal, sl, ws)
         if e: e[3].record(stream)
-        fa.fa_backward_finish(dq, scale, ws)
+        fa.fa_backward_dq(q, k, v, do, lse, dq, scale, causal, sl, ws)
         if e: e[4].record(stream)
 
     for _ in range(args.warmup):
@@ -144,10 +146,11 @@ def main():
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in ev) / args.steps
 
-    ms_fwd, ms_pre, ms_main, ms_fin = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
-    ms_bwd = ms_pre + ms_main + ms_fin
+    ms_fwd, ms_pre, ms_dkdv, ms_dq = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    ms_bwd = ms_pre + ms_dkdv + ms_dq
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
-    kernels = {"fwd_bf16_kernel": (ms_fwd, flops_fwd), "bwd_main_kernel": (ms_main, flops_bwd)}
+    kernels = {"fwd_bf16_kernel": (ms_fwd, flops_fwd), "bwd_dkdv_kernel": (ms_dkdv, flops_dkdv),
+               "bwd_dq_kernel": (ms_dq, flops_dq)}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_flops = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -160,8 +163,8 @@ def main():
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(ms_fwd, 4), "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
                 "pct_of_mfma_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
-        "bwd": {"ms": round(ms_bwd, 4), "ms_prepare": round(ms_pre, 4), "ms_main": round(ms_main, 4),
-                "ms_finish": round(ms_fin, 4), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
+        "bwd": {"ms": round(ms_bwd, 4), "ms_prepare": round(ms_pre, 4), "ms_dkdv": round(ms_dkdv, 4),
+                "ms_dq": round(ms_dq, 4), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
         "flops": {"fwd": flops_fwd, "bwd": flops_bwd},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,

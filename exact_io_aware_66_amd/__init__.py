@@ -25,8 +25,8 @@ FA_OK = 0
 FA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_MISALIGNED",
           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
-EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_main",
-           "fa_backward_finish", "fa_status_string", "fa_last_error")
+EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
+           "fa_backward_dq", "fa_status_string", "fa_last_error")
 
 _lib = None
 
@@ -52,10 +52,10 @@ def load(path: str = LIB_PATH):
     lib.fa_backward.restype = i
     lib.fa_backward_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_backward_prepare.restype = i
-    lib.fa_backward_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
-    lib.fa_backward_main.restype = i
-    lib.fa_backward_finish.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
-    lib.fa_backward_finish.restype = i
+    lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_backward_dkdv.restype = i
+    lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -143,7 +143,7 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fa
 
 
 def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
-    """Stage 1 of fa_backward: D = rowsum(dO * O) (bf16: also LSE log2 e and a cleared dQ accumulator)."""
+    """Stage 1 of fa_backward: D = rowsum(dO * O) into the workspace (bf16: also LSE log2 e)."""
     lib = load()
     B, H, N, d = _dims(o)
     _same(o, do, lse, workspace)
@@ -151,26 +151,30 @@ def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def fa_backward_main(q, k, v, do, lse, dq, dk, dv, scale: float, causal: bool = False, seqlens=None,
+def fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale: float, causal: bool = False, seqlens=None,
                      workspace=None, stream=None) -> None:
-    """Stage 2 of fa_backward: the recompute pass (dK, dV, dQ accumulation)."""
+    """Stage 2 of fa_backward: the recompute pass over query blocks per key block (dK, dV)."""
     lib = load()
     B, H, N, d = _dims(q)
-    _same(q, k, v, do, lse, dq, dk, dv, workspace)
+    _same(q, k, v, do, lse, dk, dv, workspace)
     seqlens = _seqlens(seqlens, B, q.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.fa_backward_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+    _check(lib.fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
                                 B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                                 _ptr(workspace), nbytes, _stream(stream)))
 
 
-def fa_backward_finish(dq, scale: float, workspace, stream=None) -> None:
-    """Stage 3 of fa_backward (bf16): dq = scale * accumulator."""
+def fa_backward_dq(q, k, v, do, lse, dq, scale: float, causal: bool = False, seqlens=None, workspace=None,
+                   stream=None) -> None:
+    """Stage 3 of fa_backward: the recompute pass over key blocks per query block (dQ)."""
     lib = load()
-    B, H, N, d = _dims(dq)
-    _same(dq, workspace)
-    _check(lib.fa_backward_finish(_ptr(dq), B, H, N, d, float(scale), _dtype_code(dq), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    B, H, N, d = _dims(q)
+    _same(q, k, v, do, lse, dq, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq),
+                              B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
+                              _ptr(workspace), nbytes, _stream(stream)))
 
 
 def _default_scale(d: int) -> float:

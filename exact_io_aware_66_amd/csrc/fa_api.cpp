@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
+#include <utility>
 
 #include "fa_launch.hpp"
 
@@ -68,16 +70,15 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d, bool bf16) {
   w.delta_bytes = rows * sizeof(float);
   w.lse2_off = round_up(w.delta_bytes);
   w.lse2_bytes = bf16 ? rows * sizeof(float) : 0;
-  w.dqacc_off = w.lse2_off + round_up(w.lse2_bytes);
-  w.dqacc_bytes = bf16 ? (size_t)B * H * bwd_rows_padded(N) * (size_t)d * sizeof(float) : 0;
-  w.total = w.dqacc_off + round_up(w.dqacc_bytes);
+  w.total = w.lse2_off + round_up(w.lse2_bytes);
+  (void)d;
   return w;
 }
 }  // namespace fa
 
 namespace {
 
-fa_status_t check_workspace(int B, int H, int N, int d, fa_dtype_t dtype, void* workspace, size_t workspace_bytes) {
+fa_status_t check_workspace(int B, int H, int N, int d, fa_dtype_t dtype, const void* workspace, size_t workspace_bytes) {
   const size_t need = fa_backward_workspace_size(B, H, N, d, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
@@ -103,27 +104,21 @@ fa_status_t validate_prepare(const void* o, const void* dO, const float* lse, in
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
-fa_status_t validate_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
-                          void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens,
-                          fa_dtype_t dtype, void* workspace, size_t workspace_bytes) {
+// Arguments shared by the two recompute stages; `outs` are the stage's outputs.
+fa_status_t validate_stage(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           std::initializer_list<std::pair<const void*, const char*>> outs, int B, int H, int N, int d,
+                           float scale, const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
+                           size_t workspace_bytes) {
   fa_status_t s;
   if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
   if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
-      (s = check_tensor(dO, "dO")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK ||
-      (s = check_tensor(dq, "dq")) != FA_OK || (s = check_tensor(dk, "dk")) != FA_OK ||
-      (s = check_tensor(dv, "dv")) != FA_OK)
+      (s = check_tensor(dO, "dO")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK)
     return s;
+  for (const auto& o : outs)
+    if ((s = check_tensor(o.first, o.second)) != FA_OK) return s;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
-  if (dtype == FA_DTYPE_BF16 && fa::bwd_bf16_grid(B, H, N) > 0x7fffffff)
+  if (dtype == FA_DTYPE_BF16 && (fa::bwd_dkdv_bf16_grid(B, H, N) > 0x7fffffff || fa::bwd_dq_bf16_grid(B, H, N) > 0x7fffffff))
     return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
-  return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
-}
-
-fa_status_t validate_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype, void* workspace,
-                            size_t workspace_bytes) {
-  fa_status_t s;
-  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
-  if ((s = check_tensor(dq, "dq")) != FA_OK) return s;
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
@@ -137,19 +132,22 @@ fa_status_t run_prepare(const fa::Problem& p, fa_dtype_t dtype, const void* o, c
   return e == hipSuccess ? FA_OK : hip_fail(e, "backward prepare launch");
 }
 
-fa_status_t run_main(const fa::Problem& p, fa_dtype_t dtype, const void* q, const void* k, const void* v,
-                     const void* dO, const float* lse, void* dq, void* dk, void* dv, void* workspace) {
+fa_status_t run_dkdv(const fa::Problem& p, fa_dtype_t dtype, const void* q, const void* k, const void* v,
+                     const void* dO, const float* lse, void* dk, void* dv, const void* workspace) {
   hipError_t e = (dtype == FA_DTYPE_BF16)
-                     ? fa::launch_bwd_main_bf16(p, q, k, v, dO, dk, dv, workspace)
-                     : fa::launch_bwd_main_f32(p, (const float*)q, (const float*)k, (const float*)v, (const float*)dO,
-                                               lse, (float*)dq, (float*)dk, (float*)dv, workspace);
-  return e == hipSuccess ? FA_OK : hip_fail(e, "backward main launch");
+                     ? fa::launch_bwd_dkdv_bf16(p, q, k, v, dO, dk, dv, workspace)
+                     : fa::launch_bwd_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v, (const float*)dO,
+                                               lse, (float*)dk, (float*)dv, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward dK/dV launch");
 }
 
-fa_status_t run_finish(const fa::Problem& p, fa_dtype_t dtype, void* dq, void* workspace) {
-  if (dtype != FA_DTYPE_BF16) return FA_OK;
-  hipError_t e = fa::launch_bwd_finish_bf16(p, dq, workspace);
-  return e == hipSuccess ? FA_OK : hip_fail(e, "backward finish launch");
+fa_status_t run_dq(const fa::Problem& p, fa_dtype_t dtype, const void* q, const void* k, const void* v,
+                   const void* dO, const float* lse, void* dq, const void* workspace) {
+  hipError_t e = (dtype == FA_DTYPE_BF16)
+                     ? fa::launch_bwd_dq_bf16(p, q, k, v, dO, dq, workspace)
+                     : fa::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v, (const float*)dO,
+                                             lse, (float*)dq, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward dQ launch");
 }
 
 }  // namespace
@@ -201,15 +199,15 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
                         void* stream) {
   g_last_error[0] = '\0';
   fa_status_t s;
-  if ((s = validate_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, workspace,
-                         workspace_bytes)) != FA_OK)
+  if ((s = validate_stage(q, k, v, dO, lse, {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}}, B, H, N, d, scale, seqlens, dtype,
+                          workspace, workspace_bytes)) != FA_OK)
     return s;
   if ((s = check_tensor(o, "o")) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
   const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
-  if ((s = run_main(p, dtype, q, k, v, dO, lse, dq, dk, dv, workspace)) != FA_OK) return s;
-  return run_finish(p, dtype, dq, workspace);
+  if ((s = run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace)) != FA_OK) return s;
+  return run_dq(p, dtype, q, k, v, dO, lse, dq, workspace);
 }
 
 fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -221,26 +219,28 @@ fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse,
   return run_prepare(problem(B, H, N, d, 1.f, 0, nullptr, stream), dtype, o, dO, lse, workspace);
 }
 
-fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
-                             void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                             const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+fa_status_t fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk,
+                             void* dv, int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens,
+                             fa_dtype_t dtype, const void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   fa_status_t s;
-  if ((s = validate_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, workspace,
-                         workspace_bytes)) != FA_OK)
+  if ((s = validate_stage(q, k, v, dO, lse, {{dk, "dk"}, {dv, "dv"}}, B, H, N, d, scale, seqlens, dtype, workspace,
+                          workspace_bytes)) != FA_OK)
     return s;
   if ((s = check_device()) != FA_OK) return s;
-  return run_main(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dq, dk, dv, workspace);
+  return run_dkdv(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dk, dv, workspace);
 }
 
-fa_status_t fa_backward_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
+                           int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens,
+                           fa_dtype_t dtype, const void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   fa_status_t s;
-  if ((s = validate_finish(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes)) != FA_OK) return s;
+  if ((s = validate_stage(q, k, v, dO, lse, {{dq, "dq"}}, B, H, N, d, scale, seqlens, dtype, workspace,
+                          workspace_bytes)) != FA_OK)
+    return s;
   if ((s = check_device()) != FA_OK) return s;
-  return run_finish(problem(B, H, N, d, scale, 0, nullptr, stream), dtype, dq, workspace);
+  return run_dq(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dq, workspace);
 }
 
 }  // extern "C"

@@ -1,0 +1,267 @@
+// dQ of the backward of exact attention, bf16 inputs, fp32 accumulation, on gfx950 matrix cores.
+//
+// dQ = scale dS K with dS = P * (dP - D), P = exp(S - LSE), S = scale Q K^T, dP = dO V^T: the
+// probabilities are recomputed block by block from the stored per-row log-sum-exp, never read
+// from a stored N x N matrix (NOTE-005: FlashAttention, "Method").  This kernel walks the key
+// blocks of a block of queries, like the forward, and writes dQ once, so no two workgroups ever
+// add into the same dQ row: dK and dV come from the key-block-outer kernel (fa_bwd_bf16.hip),
+// which therefore needs no atomic additions.  (Float atomics execute at the memory side on this
+// GPU at roughly 300 G operations/s; accumulating dQ that way made the backward bound by them.)
+//
+// gfx950 design (shared with the forward kernel):
+//   * one workgroup = 4 waves = 128 query rows of one (batch, head); a wave owns 32 rows and fits
+//     in 256 registers, so two workgroups share a compute unit and cover each other's stalls;
+//   * Q^T and dO^T of the wave stay in registers as B operands of S^T = K Q^T and dP^T = V dO^T
+//     (v_mfma_f32_32x32x16_bf16); each lane holds one query column, so LSE and D are one scalar
+//     per lane;
+//   * K and V tiles of 64 keys are double-buffered in LDS with direct global->LDS loads; K is read
+//     twice: row-major for S^T and through the transposing read for dQ^T += K^T dS^T;
+//   * dS^T goes from registers straight into the B operand of the dQ^T product (the key order
+//     inside each 16-key step is permuted the same way on both operands);
+//   * tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden scores to
+//     -inf first; workgroups are ordered heaviest first and, when B*H is a multiple of 8, all
+//     query blocks of one head go to one XCD.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kDqWaves = 4;
+constexpr int kDqRowsPerWave = 32;
+constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // 128 query rows per workgroup
+constexpr int kDqBc = 64;                         // keys per tile
+
+template <int D, bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                                                        const float* __restrict__ LSE2,
+                                                        const float* __restrict__ DELTA, __bf16* __restrict__ dQ,
+                                                        int H, int N, float scale, float c_log2,
+                                                        const int32_t* __restrict__ seqlens, int nqb, int BH) {
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int TILE = kDqBc * D * 2;      // bytes of one K or V tile
+  constexpr int LOADS = kDqBc * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int DS = D / 16;               // k-steps of S^T = K Q^T
+  constexpr int DT = D / 32;               // 32-wide d tiles of dQ^T
+  __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
+  FA_LDS char* kbuf0 = (FA_LDS char*)kbuf0_raw;
+  FA_LDS char* kbuf1 = (FA_LDS char*)kbuf1_raw;
+  FA_LDS char* vbuf0 = (FA_LDS char*)vbuf0_raw;
+  FA_LDS char* vbuf1 = (FA_LDS char*)vbuf1_raw;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item: (query block, batch*head), heaviest first, XCD-local heads
+  const int wid = blockIdx.x;
+  int rank, bh;
+  if ((BH & 7) == 0) {
+    const int hpx = BH >> 3;
+    const int j = wid >> 3;
+    rank = j / hpx;
+    bh = (wid & 7) + 8 * (j - rank * hpx);
+  } else {
+    rank = wid / BH;
+    bh = wid - rank * BH;
+  }
+  const int qblock = CAUSAL ? (nqb - 1 - rank) : rank;
+  const int b = bh / H;
+  const int64_t row0 = (int64_t)bh * N;
+  const __bf16* Qh = Q + row0 * D;
+  const __bf16* Kh = K + row0 * D;
+  const __bf16* Vh = V + row0 * D;
+  const __bf16* dOh = dO + row0 * D;
+
+  const int L = PADDED ? clamp_len(seqlens, b, N) : N;  // keys >= L are invisible
+  const int q0 = qblock * kDqBr;
+  const int qw = q0 + wave * kDqRowsPerWave;
+  const int kv_end = CAUSAL ? min(L, q0 + kDqBr) : L;
+  const int ntiles = (kv_end + kDqBc - 1) / kDqBc;  // tiles the workgroup loads
+  const int wave_end = CAUSAL ? min(L, qw + kDqRowsPerWave) : L;
+  const int n_wave = (wave_end + kDqBc - 1) / kDqBc;  // tiles this wave computes
+  int n_full = L / kDqBc;                             // leading tiles with no hidden pair
+  if (CAUSAL) n_full = min(n_full, qw / kDqBc);
+
+  // Q^T and dO^T fragments (B operands): lane holds query qw + l32, d = 16 ds + 8 half .. +7
+  const int query = qw + l32;
+  const int qrow = min(query, N - 1);
+  bf16x8 qf[DS], gf[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qf[ds] = *(const bf16x8*)(Qh + (int64_t)qrow * D + 16 * ds + 8 * half);
+    gf[ds] = *(const bf16x8*)(dOh + (int64_t)qrow * D + 16 * ds + 8 * half);
+  }
+  const float lse2 = LSE2[row0 + qrow];  // LSE log2(e) of this lane's query
+  const float del = DELTA[row0 + qrow];  // D = sum_c dO_c O_c
+
+  f32x16 acc[DT];  // dQ^T [d][q]: lane = query column, rows d = 32 dt + 8 (r/4) + 4 half + r%4
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+
+  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+      const int slot = (n * kDqWaves + wave) * 64;
+      const int p = slot + lane;
+      const int r = p / CH;
+      const int c = (p % CH) ^ swz<D>(r);
+      const int key = min(t * kDqBc + r, N - 1);  // rows past N are masked; read a valid row
+      gload_lds16(src + (int64_t)key * D + 8 * c, dst + slot * 16);
+    }
+  };
+
+  const int g = lane >> 4, j = lane & 15;
+  const int trow = 4 * (g >> 1) + (j >> 2);
+
+  // One 32-key half kt of a key tile: S^T, dP^T (MFMA) -> P^T, dS^T (VALU) -> dQ^T += K^T dS^T
+  // (MFMA).  The halves run one after the other so that a wave's live state fits the register
+  // budget of two waves per SIMD; the other workgroup on the compute unit fills the gaps.
+  auto half_tile = [&](int t, int kt, const FA_LDS char* kb, const FA_LDS char* vb) __attribute__((always_inline)) {
+    f32x16 s = zero16(), dp = zero16();
+    bf16x8 fk[3], fv[3];
+    auto rd = [&](int ds, bf16x8& k, bf16x8& v) {
+      const uint32_t off = tile_off<D>(32 * kt + l32, 16 * ds + 8 * half);
+      k = lds_read_b128(kb, off);
+      v = lds_read_b128(vb, off);
+    };
+    rd(0, fk[0], fv[0]);
+    rd(1, fk[1], fv[1]);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ds + 2 < DS) rd(ds + 2, fk[(ds + 2) % 3], fv[(ds + 2) % 3]);
+      s = mfma32x32x16(fk[ds % 3], qf[ds], s);
+      dp = mfma32x32x16(fv[ds % 3], gf[ds], dp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // P^T = exp2(S^T c - LSE log2 e), hidden pairs 0; dS^T = P^T (dP^T - D), packed to bf16 in the
+    // B-operand key order of the dQ^T product
+    float cf = c_log2;
+    float sv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = s[r];
+    if (t >= n_full) {
+      const int key0 = t * kDqBc + 32 * kt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = (key < L) & (!CAUSAL | (key <= query));
+        sv[r] = vis ? sv[r] * c_log2 : -INFINITY;
+      }
+      cf = 1.f;
+    }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      float d8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(sv[8 * kh + e], cf, -lse2));
+        d8[e] = p * (dp[8 * kh + e] - del);
+      }
+      dsb[kh] = pack8f(d8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // dQ^T += K^T dS^T: K^T fragment (lane: d = 32 dt + l32; keys 16 ks + 4 half + 0..3 and
+    // 16 ks + 8 + 4 half + 0..3) from two transposing reads (bases for rows trow and trow + 8)
+    bf16x8 fa[3];
+    auto rdk = [&](int i, bf16x8& a) {
+      const int dt = i >> 1, ks = 2 * kt + (i & 1);
+      const uint32_t b0 = tile_off<D>(trow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+      const uint32_t b8 = tile_off<D>(trow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+      a = cat(lds_read_tr(kb, b0), lds_read_tr(kb, b8));
+    };
+    rdk(0, fa[0]);
+    rdk(1, fa[1]);
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < 2 * DT) rdk(i + 2, fa[(i + 2) % 3]);
+      acc[i >> 1] = mfma32x32x16(fa[i % 3], dsb[i & 1], acc[i >> 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto tile = [&](int t, const FA_LDS char* kb, const FA_LDS char* vb) __attribute__((always_inline)) {
+    half_tile(t, 0, kb, vb);
+    half_tile(t, 1, kb, vb);
+  };
+
+  if (ntiles > 0) {
+    load_tile(Kh, 0, kbuf0);
+    load_tile(Vh, 0, vbuf0);
+  }
+  // tile t in buffers t%2; the load of tile t+1 goes into the other pair, read last in iteration t-1
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      load_tile(Kh, t + 1, kbuf1);
+      load_tile(Vh, t + 1, vbuf1);
+    }
+    if (t < n_wave) tile(t, kbuf0, vbuf0);
+    if (t + 1 < ntiles) {
+      wait_vmem();
+      __syncthreads();
+      if (t + 2 < ntiles) {
+        load_tile(Kh, t + 2, kbuf0);
+        load_tile(Vh, t + 2, vbuf0);
+      }
+      if (t + 1 < n_wave) tile(t + 1, kbuf1, vbuf1);
+    }
+  }
+
+  // ---- epilogue: dQ = scale acc (bf16, RNE); lane holds query `query`, d = 32 dt + 8 gq + 4 half + 0..3
+  if (query < N) {
+    __bf16* drow = dQ + (row0 + query) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dt + 8 * gq + 4 * half;
+        *(bf16x4*)(drow + d0) = pack4(acc[dt][4 * gq] * scale, acc[dt][4 * gq + 1] * scale,
+                                      acc[dt][4 * gq + 2] * scale, acc[dt][4 * gq + 3] * scale);
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool PADDED>
+hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                  const float* delta, void* dq) {
+  const int nqb = (p.N + kDqBr - 1) / kDqBr;
+  const int BH = p.B * p.H;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta, (__bf16*)dq,
+                     p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, nqb, BH);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                    const float* delta, void* dq) {
+  const bool pad = p.seqlens != nullptr;
+  if (p.causal)
+    return pad ? launch<D, true, true>(p, q, k, v, dO, lse2, delta, dq) : launch<D, true, false>(p, q, k, v, dO, lse2, delta, dq);
+  return pad ? launch<D, false, true>(p, q, k, v, dO, lse2, delta, dq) : launch<D, false, false>(p, q, k, v, dO, lse2, delta, dq);
+}
+
+}  // namespace
+
+int64_t bwd_dq_bf16_grid(int B, int H, int N) { return (int64_t)((N + kDqBr - 1) / kDqBr) * B * H; }
+
+hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO, void* dq,
+                              const void* workspace) {
+  const BwdWorkspace ws = bwd_workspace_layout(p.B, p.H, p.N, p.d, true);
+  const float* delta = (const float*)((const char*)workspace + ws.delta_off);
+  const float* lse2 = (const float*)((const char*)workspace + ws.lse2_off);
+  return p.d == 64 ? launch_d<64>(p, q, k, v, dO, lse2, delta, dq) : launch_d<128>(p, q, k, v, dO, lse2, delta, dq);
+}
+
+}  // namespace fa

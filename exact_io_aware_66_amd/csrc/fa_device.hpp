@@ -161,6 +161,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   return cat(lo, hi);
 }
 
+// 8 consecutive floats of an array -> 8 bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8f(const float* v, int base) {
+  f32x2 a = {v[base + 0], v[base + 1]}, b = {v[base + 2], v[base + 3]};
+  f32x2 c = {v[base + 4], v[base + 5]}, d = {v[base + 6], v[base + 7]};
+  bf16x2 pa = __builtin_convertvector(a, bf16x2), pb = __builtin_convertvector(b, bf16x2);
+  bf16x2 pc = __builtin_convertvector(c, bf16x2), pd = __builtin_convertvector(d, bf16x2);
+  return cat(__builtin_shufflevector(pa, pb, 0, 1, 2, 3), __builtin_shufflevector(pc, pd, 0, 1, 2, 3));
+}
+
 __device__ __forceinline__ bf16x4 pack4(float a0, float a1, float a2, float a3) {
   f32x2 a = {a0, a1}, b = {a2, a3};
   bf16x2 pa = __builtin_convertvector(a, bf16x2), pb = __builtin_convertvector(b, bf16x2);

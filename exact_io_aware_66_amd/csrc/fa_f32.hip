@@ -231,13 +231,18 @@ hipError_t fwd(const Problem& p, const float* q, const float* k, const float* v,
 }
 
 template <int D, bool CAUSAL>
-hipError_t bwd(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
-               const float* delta, float* dq, float* dk, float* dv) {
+hipError_t bwd_kv(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                  const float* delta, float* dk, float* dv) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dk, dv,
                      p.H, p.N, p.scale, p.seqlens);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_q(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                 const float* delta, float* dq) {
+  dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dq, p.H,
                      p.N, p.scale, p.seqlens);
   return hipGetLastError();
@@ -250,15 +255,24 @@ hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, cons
   return p.causal ? fwd<128, true>(p, q, k, v, o, lse) : fwd<128, false>(p, q, k, v, o, lse);
 }
 
-hipError_t launch_bwd_main_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
-                               const float* lse, float* dq, float* dk, float* dv, void* workspace) {
+hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
+                               const float* lse, float* dk, float* dv, const void* workspace) {
   const BwdWorkspace ws = bwd_workspace_layout(p.B, p.H, p.N, p.d, false);
-  const float* delta = (const float*)((char*)workspace + ws.delta_off);
+  const float* delta = (const float*)((const char*)workspace + ws.delta_off);
   if (p.d == 64)
-    return p.causal ? bwd<64, true>(p, q, k, v, dO, lse, delta, dq, dk, dv)
-                    : bwd<64, false>(p, q, k, v, dO, lse, delta, dq, dk, dv);
-  return p.causal ? bwd<128, true>(p, q, k, v, dO, lse, delta, dq, dk, dv)
-                  : bwd<128, false>(p, q, k, v, dO, lse, delta, dq, dk, dv);
+    return p.causal ? bwd_kv<64, true>(p, q, k, v, dO, lse, delta, dk, dv)
+                    : bwd_kv<64, false>(p, q, k, v, dO, lse, delta, dk, dv);
+  return p.causal ? bwd_kv<128, true>(p, q, k, v, dO, lse, delta, dk, dv)
+                  : bwd_kv<128, false>(p, q, k, v, dO, lse, delta, dk, dv);
+}
+
+hipError_t launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
+                             const float* lse, float* dq, const void* workspace) {
+  const BwdWorkspace ws = bwd_workspace_layout(p.B, p.H, p.N, p.d, false);
+  const float* delta = (const float*)((const char*)workspace + ws.delta_off);
+  if (p.d == 64)
+    return p.causal ? bwd_q<64, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q<64, false>(p, q, k, v, dO, lse, delta, dq);
+  return p.causal ? bwd_q<128, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q<128, false>(p, q, k, v, dO, lse, delta, dq);
 }
 
 }  // namespace fa

@@ -10,8 +10,9 @@
 //
 // gfx950 design (the pages' A100 tile rule B_c = ceil(M/4d), B_r = min(B_c, d) is not used; the
 // tile is set by the register file, LDS and issue model of a CDNA4 compute unit):
-//   * one workgroup = 4 waves = 256 query rows of one (batch, head), one wave per SIMD; a wave owns
-//     64 rows, so every K/V byte read from LDS feeds 64 query rows;
+//   * one workgroup = 4 waves of one (batch, head), one wave per SIMD; a wave owns 32 query rows
+//     (128 per workgroup), fits in 256 registers, and two workgroups share a compute unit so each
+//     covers the other's memory and barrier stalls (64 rows per wave is a compile-time option);
 //   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16);
 //     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
 //     lane halves hold different keys of the same queries and are combined once, at the end);
@@ -19,8 +20,9 @@
 //     global->LDS 16-byte loads; K runs one tile ahead of V, so each load has a full iteration to
 //     land before it is read;
 //   * software pipeline: S(t+1) = K(t+1) Q^T is issued on the matrix cores while the VALU turns
-//     S(t) into P(t) (exp2, bf16 pack, row sums), the two instruction streams interleaved by
-//     sched_group_barrier; then O^T += V(t)^T P(t)^T, with V^T read through ds_read_b64_tr_b16;
+//     S(t) into P(t) (exp2, bf16 pack, row sums) and O^T += V(t-1)^T P(t-1)^T runs beside it; the
+//     instruction streams are interleaved by explicit schedule groups, LDS fragments are read two
+//     MFMA steps ahead, and V^T is read through ds_read_b64_tr_b16;
 //   * lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by more
 //     than 2^8 (base 2), so p <= 2^8 and the output/normaliser, which share the stale maximum, stay
 //     exact; the O rescale (128 accumulator registers) therefore runs a few times per row instead of

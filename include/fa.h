@@ -78,8 +78,7 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes: one float32 per row for
- * D_i = sum_c dO_ic O_ic, plus (bf16 only) one float32 per row for LSE_i log2(e) and a float32
- * [B][H][Npad][d] accumulator for dQ, Npad = N rounded up to a multiple of 64.  Returns 0 for
+ * D_i = sum_c dO_ic O_ic, plus (bf16 only) one float32 per row for LSE_i log2(e).  Returns 0 for
  * invalid or unsupported sizes.  Linear in N (O(N) extra memory; NOTE-005 "Key results",
  * Theorem 1).
  */
@@ -90,10 +89,9 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d, fa_dtype_t dtype);
  *   o, lse must be exactly what fa_forward returned for the same q, k, v, sizes, scale, causal
  *   and seqlens (not checked; otherwise the result is undefined).
  *   workspace: caller-owned device memory of at least fa_backward_workspace_size() bytes,
- *   16-byte aligned; the library clears what it needs itself.  Its contents are scratch.
- * The attention block is recomputed from Q, K and LSE (NOTE-005 "Method"); dQ is accumulated
- * across key blocks with float32 atomic adds, so its last bits may differ between runs, while
- * dk and dv are bitwise reproducible.
+ *   16-byte aligned; its contents on entry do not matter and are scratch on exit.
+ * The attention block is recomputed from Q, K and LSE (NOTE-005 "Method").  Every output element
+ * has a single writer and a fixed summation order, so dq, dk and dv are bitwise reproducible.
  */
 fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* o,
                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
@@ -104,23 +102,26 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
 /*
  * The backward in its three stages, for callers that schedule or time them separately.
  * fa_backward(...) is exactly these three calls in order on one stream, with the same workspace:
- *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; for bf16 also LSE_i log2(e)
- *                         and a cleared dQ accumulator.  Reads o, dO and lse only.
- *   fa_backward_main    : the recompute pass over key blocks: writes dk, dv, and accumulates dQ
- *                         (bf16: into the workspace; float32: straight into dq).  Needs the
- *                         workspace as fa_backward_prepare left it.
- *   fa_backward_finish  : bf16 only: dq = scale * (dQ accumulator), rounded to bf16.  No work for
- *                         float32 (returns FA_OK).
+ *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; for bf16 also LSE_i log2(e).
+ *                         Reads o, dO and lse only.
+ *   fa_backward_dkdv    : the recompute pass over query blocks for each block of keys: writes dk
+ *                         and dv.  Reads the workspace as fa_backward_prepare left it.
+ *   fa_backward_dq      : the recompute pass over key blocks for each block of queries: writes dq.
+ *                         Reads the workspace as fa_backward_prepare left it.
+ * fa_backward_dkdv and fa_backward_dq do not depend on each other (both only read the workspace),
+ * so they may run in either order or on two streams once fa_backward_prepare has completed.
  * Arguments, layout and errors as in fa_backward.
  */
 fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                                 fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
-fa_status_t fa_backward_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                             void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                             int causal, const int32_t* seqlens, fa_dtype_t dtype, void* workspace,
+fa_status_t fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                             void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                             const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
                              size_t workspace_bytes, void* stream);
-fa_status_t fa_backward_finish(void* dq, int B, int H, int N, int d, float scale, fa_dtype_t dtype,
-                               void* workspace, size_t workspace_bytes, void* stream);
+fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           void* dq, int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t status);

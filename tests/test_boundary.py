@@ -79,8 +79,9 @@ def test_backward_argument_errors(lib, kw, code):
 def test_workspace_size_is_linear_in_n(lib):
     sizes = [lib.fa_backward_workspace_size(2, 16, n, 128, BF16) for n in (1024, 2048, 4096)]
     assert sizes[1] > sizes[0] > 0 and sizes[2] - sizes[1] == 2 * (sizes[1] - sizes[0])
-    # bf16: fp32 D row statistic + fp32 dQ accumulator; fp32 inputs: the row statistic only
-    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, BF16) >= 2 * 16 * 4096 * (4 + 128 * 4)
+    # bf16: fp32 D and LSE log2(e) row statistics; fp32 inputs: D only
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, BF16) >= 2 * 16 * 4096 * 8
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128, BF16) < 2 * 16 * 4096 * 12
     assert lib.fa_backward_workspace_size(2, 16, 4096, 128, F32) >= 2 * 16 * 4096 * 4
     assert lib.fa_backward_workspace_size(2, 16, 4096, 128, F32) < 2 * 16 * 4096 * 8
     assert lib.fa_backward_workspace_size(0, 16, 4096, 128, BF16) == 0
