@@ -60,6 +60,13 @@ fa_status_t check_f32_vec(const void* p, const char* name) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The bf16 kernels address one head's rows through 32-bit buffer offsets.
+fa_status_t check_head_bytes(int N, int d, fa_dtype_t dtype) {
+  if (dtype == FA_DTYPE_BF16 && (int64_t)N * d * 2 > 0x7fffffff)
+    return fail(FA_ERR_INVALID_ARGUMENT, "N*d*2 (bytes of one head) must be below 2^31 for bf16 (N=%d, d=%d)", N, d);
+  return FA_OK;
+}
+
 }  // namespace
 
 namespace fa {
@@ -119,6 +126,7 @@ fa_status_t validate_stage(const void* q, const void* k, const void* v, const vo
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
   if (dtype == FA_DTYPE_BF16 && (fa::bwd_dkdv_bf16_grid(B, H, N) > 0x7fffffff || fa::bwd_dq_bf16_grid(B, H, N) > 0x7fffffff))
     return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
+  if ((s = check_head_bytes(N, d, dtype)) != FA_OK) return s;
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
@@ -182,9 +190,10 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
       (s = check_tensor(o, "o")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK)
     return s;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
-  if ((s = check_device()) != FA_OK) return s;
   if (dtype == FA_DTYPE_BF16 && fa::fwd_bf16_grid(B, H, N) > 0x7fffffff)
-    return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/256) must be below 2^31");
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
+  if ((s = check_head_bytes(N, d, dtype)) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
   const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   const hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, q, k, v, o, lse)
                                : fa::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse);

@@ -24,6 +24,8 @@
 //             scores to -inf first (so P = 0 and dS = 0 there).
 // dQ comes from a query-block-outer kernel of its own (fa_bwd_dq.hip), so that every output row has
 // exactly one writer and no atomic additions are needed anywhere in the backward.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -78,15 +80,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   constexpr int LOADS = BR * CH / 256;        // 16-byte loads per thread per tile and tensor
   constexpr int DS = D / 16;                  // k-steps over d
   constexpr int DT = D / 32;                  // 32-wide d tiles
-  constexpr int STAGE = 2 * QTILE + 2 * 64 * 4;  // Q | dO | LSE log2 e (64 floats) | D (64 floats)
-  // Separate, statically referenced LDS arrays (as in the forward kernel): a direct load into one
-  // stage is then never taken to alias the reads of another.
+  constexpr int STAGE = 2 * QTILE + 4 * 256;  // Q | dO | per-wave row statistics: LSE log2 e, D, LSE, D
+  constexpr int VMEM_PER_TILE = 2 * LOADS + 1;  // vector-memory instructions per wave per tile
+  // Leading query tiles that cross the causal diagonal of the block's 128 keys; every later tile is
+  // fully visible to every key of the block.
+  constexpr int HEAD = CAUSAL ? kBwdBc / BR : 0;
+  // Four separate, statically referenced LDS stages (as in the forward kernel, a direct load into one
+  // stage is then never taken to alias the reads of another): tile u lives in stage u % 4.
   __shared__ __attribute__((aligned(1024))) char st0_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2_raw[STAGE];
-  FA_LDS char* st0 = (FA_LDS char*)st0_raw;
-  FA_LDS char* st1 = (FA_LDS char*)st1_raw;
-  FA_LDS char* st2 = (FA_LDS char*)st2_raw;
+  __shared__ __attribute__((aligned(1024))) char st3_raw[STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -114,8 +118,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   const __bf16* Kh = K + row0 * D;
   const __bf16* Vh = V + row0 * D;
   const __bf16* dOh = dO + row0 * D;
-  const float* LSEh = LSE2 + row0;
-  const float* DELh = DELTA + row0;
 
   const int L = PADDED ? clamp_len(seqlens, b, N) : N;
   const int k0 = kblock * kBwdBc;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     // ---- stationary operands: K and V rows of this wave's keys (B operands of S and dP)
     bf16x8 kb[DS], vb[DS];
     {
-      const int key = min(my_key, N - 1);  // keys past N are masked
+      const int key = min(my_key, N - 1);  // keys past N are never written back
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         kb[ds] = *(const bf16x8*)(Kh + (int64_t)key * D + 16 * ds + 8 * half);
@@ -146,30 +148,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     const int it0 = CAUSAL ? (k0 / BR) : 0;
     const int count = nqt - it0;  // query tiles this key block visits (>= 1)
 
+    // Tile loads: buffer loads straight into LDS.  Rows past N read as zeros (the buffer ends at the
+    // head's last row), and a zero Q and dO row adds exactly nothing to dK and dV, so the ragged last
+    // tile needs no mask.  Per-lane byte offsets inside a tile are loop-invariant.
+    uint32_t voff[LOADS];
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+      const int p = (n * kBwdWaves + wave) * 64 + lane;
+      const int r = p / CH;
+      const int c = (p % CH) ^ swz<D>(r);
+      voff[n] = (uint32_t)(r * D + 8 * c) * 2;
+    }
+    // Wave w fetches 64 rows of statistic w & 1 (0: LSE log2 e, 1: D) into its own 256-byte slot.
+    const float* stat = (wave & 1) ? DELTA + row0 : LSE2 + row0;
     auto load_tile = [&](int u, FA_LDS char* dst) {
       const int qbase = (it0 + u) * BR;
+      const int left = N - qbase;  // rows of the head from qbase on (>= 1)
+      const u32x4 rq = make_rsrc(Qh + (int64_t)qbase * D, left * D * 2);
+      const u32x4 rg = make_rsrc(dOh + (int64_t)qbase * D, left * D * 2);
 #pragma unroll
       for (int n = 0; n < LOADS; ++n) {
         const int slot = (n * kBwdWaves + wave) * 64;
-        const int p = slot + lane;
-        const int r = p / CH;
-        const int c = (p % CH) ^ swz<D>(r);
-        const int q = min(qbase + r, N - 1);
-        gload_lds16(Qh + (int64_t)q * D + 8 * c, dst + slot * 16);
-        gload_lds16(dOh + (int64_t)q * D + 8 * c, dst + QTILE + slot * 16);
+        bload_lds16(rq, voff[n], dst + slot * 16);
+        bload_lds16(rg, voff[n], dst + QTILE + slot * 16);
       }
-      if (wave < 2) {  // 64 rows of LSE log2 e / D; rows past the tile are clamped and unused
-        const int q = min(qbase + lane, N - 1);
-        gload_lds4(wave == 0 ? (const void*)(LSEh + q) : (const void*)(DELh + q), dst + 2 * QTILE + wave * 256);
-      }
+      bload_lds4(make_rsrc(stat + qbase, left * 4), lane * 4, dst + 2 * QTILE + wave * 256);
     };
 
-    f32x16 s[QS], dp[QS];  // S and dP of a tile: lane = key my_key, rows = queries
+    // S and dP of two consecutive tiles (set u % 2 holds tile u): lane = key my_key, rows = queries
+    f32x16 s[2][QS], dp[2][QS];
 
-    // S = Q K^T and dP = dO V^T for the tile in st, DS k-steps of 2 QS MFMAs.  The A operands are
-    // read row-major from LDS two k-steps ahead (a ring of three fragment sets); `between(ds)`
-    // places other work after the MFMAs of k-step ds.
-    auto scores = [&](const FA_LDS char* st, auto&& between) {
+    // S = Q K^T and dP = dO V^T for the tile in st into set P, DS k-steps of 2 QS MFMAs.  The A
+    // operands are read row-major from LDS two k-steps ahead (a ring of three fragment sets);
+    // `between(ds)` places other work after the MFMAs of k-step ds.
+    auto scores = [&](auto par, const FA_LDS char* st, auto&& between) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
       bf16x8 fq[3][QS], fd[3][QS];
       auto rd = [&](int ds, bf16x8 (&q)[QS], bf16x8 (&d)[QS]) {
 #pragma unroll
@@ -181,8 +194,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       };
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        s[qs] = zero16();
-        dp[qs] = zero16();
+        s[P][qs] = zero16();
+        dp[P][qs] = zero16();
       }
       rd(0, fq[0], fd[0]);
       if (DS > 1) rd(1, fq[1], fd[1]);
@@ -192,50 +205,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         if (ds + 2 < DS) rd(ds + 2, fq[(ds + 2) % 3], fd[(ds + 2) % 3]);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
-          s[qs] = mfma32x32x16(fq[ds % 3][qs], kb[ds], s[qs]);
-          dp[qs] = mfma32x32x16(fd[ds % 3][qs], vb[ds], dp[qs]);
+          s[P][qs] = mfma32x32x16(fq[ds % 3][qs], kb[ds], s[P][qs]);
+          dp[P][qs] = mfma32x32x16(fd[ds % 3][qs], vb[ds], dp[P][qs]);
         }
         between(ds);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Working copies of S and dP of the tile being processed (the accumulators are rewritten by the
-    // next score product), with hidden pairs already at -inf in the scaled domain; cf is the factor
-    // still to apply to the copy of S.
-    float sv[QS][16], dv[QS][16];
-    float cf = c_log2;
-    auto take_scores = [&](int u) {
-      const int qi0 = (it0 + u) * BR;
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sv[qs][r] = s[qs][r];
-          dv[qs][r] = dp[qs][r];
-        }
-      cf = c_log2;
-      if ((kw + kBwdKeysPerWave > L) || (qi0 + BR > N) || (CAUSAL && kw + kBwdKeysPerWave - 1 > qi0)) {
+    bf16x8 pb[2 * QS], db[2 * QS];  // P and dS packed (B operands of dV^T and dK^T), k = queries
+
+    // One tile u (set P = u % 2, in stage cur; tile u+1 in stage nxt; tile u+3 is loaded into
+    // stage ldst).  MASK: tile u crosses the causal diagonal of this block.  Every instance is
+    // straight-line code: which tiles take the masked form is decided outside the loop.
+    auto step = [&](auto mask, auto par, int u, const FA_LDS char* cur, const FA_LDS char* nxt, FA_LDS char* ldst)
+        __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask)::value;
+      constexpr int P = decltype(par)::value;
+      // tile u+1 must have landed; tile u+2 (issued one step ago) may still be in flight
+      if (u + 2 < count) wait_vmem_n<VMEM_PER_TILE>();
+      else wait_vmem();
+      barrier();
+      if (u + 3 < count) load_tile(u + 3, ldst);
+
+      float cf = c_log2;
+      if constexpr (MASK) {  // hidden pairs (key > query) to -inf, in the scaled domain
+        const int qi0 = (it0 + u) * BR;
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int query = qi0 + 32 * qs + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = (my_key < L) & (query < N) & (!CAUSAL | (my_key <= query));
-            sv[qs][r] = vis ? sv[qs][r] * c_log2 : -INFINITY;
+            s[P][qs][r] = (my_key <= query) ? s[P][qs][r] * c_log2 : -INFINITY;
           }
         cf = 1.f;
       }
-    };
-
-    bf16x8 pb[2 * QS], db[2 * QS];  // P and dS packed (B operands of dV^T and dK^T), k = queries
-
-    // One tile: tile u in cur (Q, dO, LSE log2 e, D) with its scores in sv/dv; st_next holds tile
-    // u+1; tile u+2 is loaded into st_load.
-    auto step = [&](int u, const FA_LDS char* cur, const FA_LDS char* st_next, FA_LDS char* st_load) {
-      wait_vmem();  // tile u+1 landed (loaded two iterations ago)
-      __syncthreads();
-      if (u + 2 < count) load_tile(u + 2, st_load);
 
       // ---- C: S(u+1), dP(u+1) on the matrix cores || P(u), dS(u) on the VALU, then packed
       const FA_LDS float* lse_t = (const FA_LDS float*)(cur + 2 * QTILE);
@@ -248,14 +252,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
-          const float p = fast_exp2(fmaf(sv[qs][r], cf, -lse4[e]));
-          sv[qs][r] = p;
-          dv[qs][r] = p * (dv[qs][r] - del4[e]);
+          const float p = fast_exp2(fmaf(s[P][qs][r], cf, -lse4[e]));
+          s[P][qs][r] = p;
+          dp[P][qs][r] = p * (dp[P][qs][r] - del4[e]);
         }
       };
       auto pack = [&](int ks) {  // one 16-query k-step of P and dS
-        pb[ks] = pack8f(sv[ks >> 1], 8 * (ks & 1));
-        db[ks] = pack8f(dv[ks >> 1], 8 * (ks & 1));
+        pb[ks] = pack8(s[P][ks >> 1], 8 * (ks & 1));
+        db[ks] = pack8(dp[P][ks >> 1], 8 * (ks & 1));
       };
       // VALU items in order: 4 QS groups, then 2 QS packs, spread over the DS k-steps of the scores
       constexpr int ITEMS = 6 * QS;
@@ -268,13 +272,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
           else if (it < ITEMS) pack(it - 4 * QS);
         }
       };
-      if (u + 1 < count) {
-        scores(st_next, valu);
-      } else {
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) valu(ds);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      // (after the last tile the product reads a stale or unwritten stage; its result is unused)
+      scores(std::integral_constant<int, 1 - P>{}, nxt, valu);
 
       // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read)
       constexpr int BS = DT * 2 * QS;  // steps (dt, ks) of 2 MFMAs
@@ -297,24 +296,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         dkt[dt] = mfma32x32x16(bq[i % 3], db[ks], dkt[dt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (u + 1 < count) take_scores(u + 1);
     };
 
-    load_tile(0, st0);
-    if (count > 1) load_tile(1, st1);
+    FA_LDS char* const st[4] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw,
+                                (FA_LDS char*)st3_raw};
+    // step u with the stage ring and the score set of phase PH = u % 4 (all compile-time)
+    auto at = [&](auto mask, auto ph, int u) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph)::value;
+      step(mask, std::integral_constant<int, PH % 2>{}, u, st[PH], st[(PH + 1) % 4], st[(PH + 3) % 4]);
+    };
+    using M = std::true_type;
+    using C = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    load_tile(0, st[0]);
+    if (count > 1) load_tile(1, st[1]);
+    if (count > 2) load_tile(2, st[2]);
     wait_vmem();
-    __syncthreads();
-    scores(st0, [](int) {});
-    take_scores(0);
-    for (int u = 0; u < count; u += 3) {
-      step(u, st0, st1, st2);
-      if (u + 1 < count) step(u + 1, st1, st2, st0);
-      if (u + 2 < count) step(u + 2, st2, st0, st1);
+    barrier();
+    scores(I0{}, st[0], [](int) {});
+
+    // masked head (causal): tiles 0 .. HEAD-1
+    if constexpr (HEAD >= 1) at(M{}, I0{}, 0);
+    if constexpr (HEAD >= 2) { if (count > 1) at(M{}, I1{}, 1); }
+    if constexpr (HEAD >= 3) { if (count > 2) at(M{}, I2{}, 2); }
+    if constexpr (HEAD >= 4) { if (count > 3) at(M{}, I3{}, 3); }
+    // fully visible tiles, four per iteration so that stages and score sets stay compile-time
+    constexpr int PH0 = HEAD % 4;
+    int u = HEAD;
+    for (; u + 3 < count; u += 4) {
+      at(C{}, std::integral_constant<int, PH0>{}, u);
+      at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
+      at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
+      at(C{}, std::integral_constant<int, (PH0 + 3) % 4>{}, u + 3);
     }
+    if (u < count) at(C{}, std::integral_constant<int, PH0>{}, u);
+    if (u + 1 < count) at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
+    if (u + 2 < count) at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
   }
 
-  // ---- dK = scale dS^T Q, dV: lane holds key my_key, d = 32 dt + 8 gq + 4 half + 0..3
+  // ---- dK = scale dS^T Q, dV: lane holds key my_key, d = 32 dt + 8 gq + 4 half + 0..3.  Keys at
+  // or past the valid length are hidden from every query: their gradients are zero (selected, not
+  // multiplied: their unmasked accumulators may hold any value).
   if (my_key < N) {
+    const bool live = !PADDED || my_key < L;
     __bf16* dkrow = dK + (row0 + my_key) * D;
     __bf16* dvrow = dV + (row0 + my_key) * D;
 #pragma unroll
@@ -322,9 +350,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = 32 * dt + 8 * gq + 4 * half;
-        *(bf16x4*)(dkrow + d0) = pack4(dkt[dt][4 * gq] * scale, dkt[dt][4 * gq + 1] * scale,
-                                       dkt[dt][4 * gq + 2] * scale, dkt[dt][4 * gq + 3] * scale);
-        *(bf16x4*)(dvrow + d0) = pack4(dvt[dt][4 * gq], dvt[dt][4 * gq + 1], dvt[dt][4 * gq + 2], dvt[dt][4 * gq + 3]);
+        float kx[4], vx[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kx[e] = live ? dkt[dt][4 * gq + e] * scale : 0.f;
+          vx[e] = live ? dvt[dt][4 * gq + e] : 0.f;
+        }
+        *(bf16x4*)(dkrow + d0) = pack4(kx[0], kx[1], kx[2], kx[3]);
+        *(bf16x4*)(dvrow + d0) = pack4(vx[0], vx[1], vx[2], vx[3]);
       }
   }
 }

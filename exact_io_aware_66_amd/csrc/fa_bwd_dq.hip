@@ -14,7 +14,7 @@
 //   * Q^T and dO^T of the wave stay in registers as B operands of S^T = K Q^T and dP^T = V dO^T
 //     (v_mfma_f32_32x32x16_bf16); each lane holds one query column, so LSE and D are one scalar
 //     per lane;
-//   * K and V tiles of 64 keys are double-buffered in LDS with direct global->LDS loads; K is read
+//   * K and V tiles of 64 keys are double-buffered in LDS with direct buffer->LDS loads; K is read
 //     twice: row-major for S^T and through the transposing read for dQ^T += K^T dS^T;
 //   * dS^T goes from registers straight into the B operand of the dQ^T product (the key order
 //     inside each 16-key step is permuted the same way on both operands);
@@ -104,16 +104,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
-  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+  // K/V tile loads: buffer loads straight into LDS; rows past N read as zeros (the buffer ends at
+  // the head's last row; those keys are masked).  Per-lane byte offsets inside a tile are
+  // loop-invariant.
+  uint32_t voff[LOADS];
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int slot = (n * kDqWaves + wave) * 64;
-      const int p = slot + lane;
-      const int r = p / CH;
-      const int c = (p % CH) ^ swz<D>(r);
-      const int key = min(t * kDqBc + r, N - 1);  // rows past N are masked; read a valid row
-      gload_lds16(src + (int64_t)key * D + 8 * c, dst + slot * 16);
-    }
+  for (int n = 0; n < LOADS; ++n) {
+    const int p = (n * kDqWaves + wave) * 64 + lane;
+    const int r = p / CH;
+    const int c = (p % CH) ^ swz<D>(r);
+    voff[n] = (uint32_t)(r * D + 8 * c) * 2;
+  }
+  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+    const u32x4 rs = make_rsrc(src + (int64_t)t * kDqBc * D, (N - t * kDqBc) * D * 2);
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kDqWaves + wave) * 1024);
   };
 
   const int g = lane >> 4, j = lane & 15;
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict
   // tile t in buffers t%2; the load of tile t+1 goes into the other pair, read last in iteration t-1
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
-    __syncthreads();
+    barrier();
     if (t + 1 < ntiles) {
       load_tile(Kh, t + 1, kbuf1);
       load_tile(Vh, t + 1, vbuf1);
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict
     if (t < n_wave) tile(t, kbuf0, vbuf0);
     if (t + 1 < ntiles) {
       wait_vmem();
-      __syncthreads();
+      barrier();
       if (t + 2 < ntiles) {
         load_tile(Kh, t + 2, kbuf0);
         load_tile(Vh, t + 2, vbuf0);

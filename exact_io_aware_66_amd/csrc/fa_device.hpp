@@ -2,7 +2,7 @@
 //
 // Everything here is specific to CDNA4 (gfx950): wave64, the bf16 matrix-core instruction
 // v_mfma_f32_32x32x16_bf16, the transposing LDS read ds_read_b64_tr_b16 and the direct
-// global->LDS load global_load_lds_dwordx4.
+// global->LDS loads (global_load_lds_dwordx4, buffer_load_dwordx4 ... lds).
 //
 // Lane layouts used by the kernels (wave64, lane l, half h = l / 32):
 //   32x32x16 MFMA  A[32][16]: lane l holds row l%32, k = 8h .. 8h+7
@@ -10,7 +10,8 @@
 //                  C[32][32]: lane l holds column l%32, rows 8(r/4) + 4h + r%4 for r = 0..15
 //   ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i%4 of the 8-byte rows
 //                  addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its group.
-//   global_load_lds_dwordx4: lane i of a wave writes its 16 bytes at LDS base + 16 i.
+//   global_load_lds_dwordx4 / buffer_load_dwordx4 lds: lane i of a wave writes its 16 bytes at
+//                  LDS base + 16 i (the base is wave-uniform, passed in M0).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -132,7 +133,49 @@ __device__ __forceinline__ void gload_lds4(const void* gptr, FA_LDS void* lds_ba
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 4, 0, 0);
 }
 
+// Buffer resource (4 SGPRs) over `bytes` bytes from a wave-uniform base: raw addressing, stride 0.
+// A buffer load whose per-lane byte offset is >= bytes returns zeros instead of touching memory, so
+// rows past the end of a tensor need neither a clamp nor a branch.  The fourth word is the
+// gfx9-family raw-buffer format.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+// 16 bytes at byte offset voff of the buffer straight into LDS at (wave-uniform) lds_base + 16 * lane
+// (buffer_load_dwordx4 ... lds, LDS base in M0).  Issued through inline assembly so that the
+// compiler does not track the asynchronous LDS write: it would otherwise wait for every
+// outstanding load (vmcnt(0)) before reads of an unrelated LDS stage.  The caller orders the
+// transfer with wait_vmem / wait_vmem_n and a barrier before any wave reads the destination.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: no compiler-generated code here relies on it
+__device__ __forceinline__ void bload_lds16(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"((uint32_t)(uintptr_t)lds_base)
+               : "memory", "m0");
+}
+// 4 bytes at byte offset voff of the buffer into LDS at (wave-uniform) lds_base + 4 * lane.
+__device__ __forceinline__ void bload_lds4(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"((uint32_t)(uintptr_t)lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory instructions of this wave are outstanding (they complete in
+// issue order for loads), i.e. everything but the last N issued has landed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Workgroup barrier without the memory fence of __syncthreads().  The fence would make the
+// compiler wait for every outstanding direct-to-LDS load (vmcnt(0)), including prefetches that are
+// meant to stay in flight across the barrier.  Callers first wait (vmcnt) for the loads whose data
+// other waves read after the barrier.  The memory clobber keeps every LDS access of the wave on
+// its side of the barrier; the LDS reads issued before it have all been consumed (and so have
+// completed) by then, so no lgkmcnt wait is needed for the stage that is reloaded after it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Value of x in lane l ^ 32 combined with x by max / add (one v_permlane32_swap).
 __device__ __forceinline__ float max_halves(float x) {

@@ -27,7 +27,8 @@
  *   q, k, v, o, dO, dq, dk, dv : contiguous row-major [B][H][N][d], d fastest, element type `dtype`.
  *   lse                        : contiguous [B][H][N] float32 (natural log, units of the scaled
  *                                scores), written by fa_forward and read by fa_backward.
- *   d must be 64 or 128.  Any N >= 1 (ragged tails are masked); offsets are 64-bit.
+ *   d must be 64 or 128.  Any N >= 1 (ragged tails are masked); offsets are 64-bit.  For bf16 the
+ *   bytes of one head, N*d*2, must be below 2^31 (FA_ERR_INVALID_ARGUMENT otherwise).
  *   Base pointers of the [B][H][N][d] tensors must be 16-byte aligned, lse and seqlens 4-byte.
  *   bf16 results are rounded to nearest even; every accumulation is float32.
  *

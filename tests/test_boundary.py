@@ -60,7 +60,7 @@ def _bwd(lib, ws=P + 65536, ws_bytes=None, B=2, H=3, N=100, d=64, dtype=BF16, sc
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(B=70000), INVALID),
     (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
     (dict(q=P + 8), MISALIGNED), (dict(o=P + 2), MISALIGNED), (dict(lse=P + 2), MISALIGNED),
-    (dict(seqlens=P + 1), MISALIGNED),
+    (dict(seqlens=P + 1), MISALIGNED), (dict(N=1 << 23, d=128), INVALID),
 ])
 def test_forward_argument_errors(lib, kw, code):
     assert _fwd(lib, **kw) == code
@@ -71,6 +71,7 @@ def test_forward_argument_errors(lib, kw, code):
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 65536 + 4), MISALIGNED),
     (dict(dq=None), INVALID), (dict(dq=P + 4), MISALIGNED), (dict(lse=None), INVALID), (dict(d=32), UNSUPPORTED),
     (dict(N=-5), INVALID), (dict(scale=float("nan")), INVALID), (dict(seqlens=P + 2), MISALIGNED),
+    (dict(N=1 << 23, d=128), INVALID),
 ])
 def test_backward_argument_errors(lib, kw, code):
     assert _bwd(lib, **kw) == code
