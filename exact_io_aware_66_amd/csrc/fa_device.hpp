@@ -139,7 +139,7 @@ __device__ __forceinline__ void gload_lds4(const void* gptr, FA_LDS void* lds_ba
 // gfx9-family raw-buffer format.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)max(bytes, 0), 0x00020000u};
 }
 // 16 bytes at byte offset voff of the buffer straight into LDS at (wave-uniform) lds_base + 16 * lane
 // (buffer_load_dwordx4 ... lds, LDS base in M0).  Issued through inline assembly so that the

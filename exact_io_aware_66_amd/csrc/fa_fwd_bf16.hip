@@ -17,7 +17,7 @@
 //     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
 //     lane halves hold different keys of the same queries and are combined once, at the end);
 //   * K and V tiles of 64 keys stream through two double-buffered LDS rings with direct
-//     global->LDS 16-byte loads; K runs one tile ahead of V, so each load has a full iteration to
+//     buffer->LDS 16-byte loads (rows past N read as zeros); K runs one tile ahead of V, so each load has a full iteration to
 //     land before it is read;
 //   * software pipeline: S(t+1) = K(t+1) Q^T is issued on the matrix cores while the VALU turns
 //     S(t) into P(t) (exp2, bf16 pack, row sums) and O^T += V(t-1)^T P(t-1)^T runs beside it; the
@@ -31,6 +31,8 @@
 //   * workgroups are ordered heaviest first (causal) and, when B*H is a multiple of 8, all query
 //     blocks of one head go to one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so a
 //     head's K/V stays in that XCD's L2.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -111,13 +113,13 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
   bf16x8 qf[QT][QLDS ? 1 : DS];
   FA_LDS char* qbuf = (FA_LDS char*)qbuf_raw + wave * (QLDS ? kFwdRowsPerWave * D * 2 : 0);
   if constexpr (QLDS) {
+    const u32x4 rq = make_rsrc(Qh + (int64_t)qw * D, (N - qw) * D * 2);  // rows past N read as zeros
 #pragma unroll
     for (int n = 0; n < kFwdRowsPerWave * CH / 64; ++n) {
       const int p = n * 64 + lane;
       const int r = p / CH;
       const int c = (p % CH) ^ swz<D>(r);
-      const int row = min(qw + r, N - 1);
-      gload_lds16(Qh + (int64_t)row * D + 8 * c, qbuf + n * 1024);
+      bload_lds16(rq, (uint32_t)(r * D + 8 * c) * 2, qbuf + n * 1024);
     }
   } else {
 #pragma unroll
@@ -147,16 +149,21 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
     l_run[qt] = 0.f;
   }
 
-  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+  // K/V tile loads: buffer loads straight into LDS; rows past N read as zeros (the buffer ends at
+  // the head's last row; those keys are masked).  K and V tiles share the per-lane byte offsets,
+  // which are loop-invariant.
+  uint32_t voff[LOADS];
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int slot = (n * kFwdWaves + wave) * 64;  // first 16-byte slot of this wave's 1 KiB
-      const int p = slot + lane;
-      const int r = p / CH;
-      const int c = (p % CH) ^ swz<D>(r);
-      const int key = min(t * kFwdBc + r, N - 1);  // rows past N are masked; read a valid row
-      gload_lds16(src + (int64_t)key * D + 8 * c, dst + slot * 16);
-    }
+  for (int n = 0; n < LOADS; ++n) {
+    const int p = (n * kFwdWaves + wave) * 64 + lane;
+    const int r = p / CH;
+    const int c = (p % CH) ^ swz<D>(r);
+    voff[n] = (uint32_t)(r * D + 8 * c) * 2;
+  }
+  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+    const u32x4 rs = make_rsrc(src + (int64_t)t * kFwdBc * D, (N - t * kFwdBc) * D * 2);
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kFwdWaves + wave) * 1024);
   };
 
   // S^T(tile in kb) = K Q^T, 4 independent accumulators, one K fragment per (ds, kt)
@@ -245,28 +252,29 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
   if (n_wave > 0) scores(kbuf0, s);
 
   // Iteration t (0 <= t <= ntiles): S(t) is in s and P(t-1) in pf.  kn holds K(t+1), vp holds V(t-1);
-  // K(t+2) is loaded into kl and V(t) into vl (both last read in iteration t-1).
-  //   prepare(t) -> [ O += P(t-1) V(t-1)  ||  P(t) = exp2(...) ] -> rescale O -> S(t+1) = K(t+1) Q^T
-  auto step = [&](int t, const FA_LDS char* kn, FA_LDS char* kl, const FA_LDS char* vp, FA_LDS char* vl) {
-    wait_vmem();
-    __syncthreads();
+  // K(t+2) is loaded into kl and V(t) into vl (both last read in iteration t-1).  Every wave runs
+  // all ntiles + 1 iterations (one barrier each) in one of four forms, chosen outside the loop so
+  // that each form is straight-line code (a data-dependent branch around in-place updates of the
+  // score registers makes the compiler copy them on every iteration):
+  //   kClean  (t < n_clean):           lazy maximum check; [O += P(t-1) V(t-1) || P(t)]; S(t+1)
+  //   kMasked (n_clean <= t < n_wave): mask + exact maximum update; the same products
+  //   kDrain  (t == n_wave):           O += P(t-1) V(t-1) only
+  //   kIdle   (t > n_wave):            only the workgroup's loads
+  // (S(t+1) is computed even when no tile t+1 follows; it is then unused.)
+  constexpr int kClean = 0, kMasked = 1, kDrain = 2, kIdle = 3;
+  auto step = [&](auto mode, int t, const FA_LDS char* kn, FA_LDS char* kl, const FA_LDS char* vp, FA_LDS char* vl)
+      __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
+    wait_vmem();  // K(t+1) and V(t-1), issued one iteration ago, have landed
+    barrier();
     if (t + 2 < ntiles) load_tile(Kh, t + 2, kl);
     if (t < ntiles) load_tile(Vh, t, vl);
-    if (t > n_wave) return;  // wave-uniform: this wave has no tile left
-    const bool do_s = t < n_wave;  // else only O += P(t-1) V(t-1) remains; P(t) is forced to 0
-
-    // ---- prepare: the lazy maximum check (fully visible tile) or mask + exact update
-    // Defaults are for the drain iteration (no P(t)): exp2(s * 1 - inf) = 0 for every s this wave can
-    // hold (finite raw scores, or the -inf of hidden pairs), so nothing is added to l.
-    float cf = 1.f, m_use[QT], alpha[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      m_use[qt] = INFINITY;
-      alpha[qt] = 1.f;
-    }
-    bool raise = false;
-    if (do_s) {
-      if (t < n_full) {
+    if constexpr (MODE == kDrain) pv(vp);
+    if constexpr (MODE == kClean || MODE == kMasked) {
+      // ---- prepare: the lazy maximum check (fully visible tile) or mask + exact update
+      float cf, m_use[QT], alpha[QT];
+      bool raise;
+      if constexpr (MODE == kClean) {
         float tm[QT];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
@@ -277,6 +285,7 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
             for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) e = NEG ? fminf(e, s[kt][qt][r]) : fmaxf(e, s[kt][qt][r]);
           e = NEG ? min_halves(e) : max_halves(e);
           tm[qt] = e * c_log2;
+          alpha[qt] = 1.f;
         }
         bool over = false;
 #pragma unroll
@@ -323,41 +332,54 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
       }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l_run[qt] *= alpha[qt];
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O += P(t-1) V(t-1) on the matrix cores, interleaved with P(t) on the VALU
-    probs(cf, m_use);
-    pv(vp);
-    // 4 DT steps of (2 transposing reads -> 2 MFMAs), each MFMA followed by its share of the VALU work
-    pipe_schedule<4 * DT, 2, QT, VALU3 / (4 * DT * QT), 2, 0>();
-    // Pin P(t) and the row sums here: without a use inside this phase the compiler sinks their
-    // computation past the matrix-core work it is meant to overlap.
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(pn[qt][ks]));
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(l_run[qt]));
-    __builtin_amdgcn_sched_barrier(0);
-    if (raise) {  // O carries P(t-1) at the old maximum: scale it to the new one
+      // ---- O += P(t-1) V(t-1) on the matrix cores, interleaved with P(t) on the VALU
+      probs(cf, m_use);
+      pv(vp);
+      // 4 DT steps of (2 transposing reads -> 2 MFMAs), each MFMA followed by its share of the VALU work
+      pipe_schedule<4 * DT, 2, QT, VALU3 / (4 * DT * QT), 2, 0>();
+      // Pin P(t) and the row sums here: without a use inside this phase the compiler sinks their
+      // computation past the matrix-core work it is meant to overlap.
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha[qt];
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(pn[qt][ks]));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(l_run[qt]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (raise) {  // O carries P(t-1) at the old maximum: scale it to the new one
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha[qt];
+      }
+      // ---- S(t+1) = K(t+1) Q^T
+      scores(kn, s);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pn[qt][ks];
     }
-    // ---- S(t+1) = K(t+1) Q^T
-    if (t + 1 < n_wave) scores(kn, s);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pn[qt][ks];
   };
-
-  for (int t = 0; t <= ntiles; t += 2) {
-    step(t, kbuf1, kbuf0, vbuf1, vbuf0);
-    if (t + 1 <= ntiles) step(t + 1, kbuf0, kbuf1, vbuf0, vbuf1);
+  // even t: K(t+1) in kbuf1, K(t+2) -> kbuf0, V(t-1) in vbuf1, V(t) -> vbuf0; odd t: the other way
+  // round.  Outside the unrolled clean loop the buffers are picked at run time (one copy of each
+  // form; two copies of the masked form would not fit the register budget).
+  auto at = [&](auto mode, int t) __attribute__((always_inline)) {
+    const bool odd = t & 1;
+    step(mode, t, odd ? kbuf0 : kbuf1, odd ? kbuf1 : kbuf0, odd ? vbuf0 : vbuf1, odd ? vbuf1 : vbuf0);
+  };
+  using Clean = std::integral_constant<int, kClean>;
+  const int n_clean = min(n_full, n_wave);
+  int t = 0;
+  for (; t + 1 < n_clean; t += 2) {
+    step(Clean{}, t, kbuf1, kbuf0, vbuf1, vbuf0);
+    step(Clean{}, t + 1, kbuf0, kbuf1, vbuf0, vbuf1);
   }
+  if (t < n_clean) step(Clean{}, t++, kbuf1, kbuf0, vbuf1, vbuf0);
+  for (; t < n_wave; ++t) at(std::integral_constant<int, kMasked>{}, t);
+  at(std::integral_constant<int, kDrain>{}, t++);  // t == n_wave <= ntiles
+  for (; t <= ntiles; ++t) at(std::integral_constant<int, kIdle>{}, t);
 
   // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
 #pragma unroll
