@@ -1,12 +1,13 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload 4] [--no-cpu-baseline]
 
 One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_dkdv,
 fa_backward_dq -- exactly what fa_backward runs) over one batch of the synthetic workload,
-inputs resident in HBM.  W untimed steps, then K timed steps bracketed by synchronisation and
-HIP events on the stream the kernels run on; per-stage HIP events inside the timed region give the
-average duration of each kernel launch.
+inputs resident in HBM.  The GPU's clocks ramp up over the first tens of milliseconds under load,
+so the step is first repeated untimed for --settle-ms (default 300 ms); then W untimed steps, then
+K timed steps bracketed by synchronisation and HIP events on the stream the kernels run on;
+per-stage HIP events inside the timed region give the average duration of each kernel launch.
 
 FLOPs are algorithmic: forward 4 d per visible (query, key) pair (QK^T and PV), backward 2.5x
 forward (QK^T recomputed, dO V^T, P^T dO, dS^T Q, dS K), of which the dK/dV pass is credited with
@@ -77,6 +78,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="repeat the step untimed for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -131,6 +134,11 @@ def main():
         fa.fa_backward_dq(q, k, v, do, lse, dq, scale, causal, sl, ws)
         if e: e[4].record(stream)
 
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -16,10 +16,11 @@
 //             d=128, 64 at d=64).  The query tiles (Q, dO, LSE log2 e, D) stream through a
 //             three-stage LDS ring filled by direct global->LDS loads two tiles ahead.  Per tile u,
 //             one barrier, then
-//               C: S(u+1) = Q K^T and dP(u+1) = dO V^T on the matrix cores, interleaved with
-//                  P(u) = exp2(S scale log2 e - LSE log2 e) and dS(u) = P (dP - D) on the VALU
-//                  (from register copies of S(u), dP(u)) and their packing to bf16;
-//               B: dV^T += dO^T P(u), dK^T += Q^T dS(u) (dO^T, Q^T through transposing LDS reads).
+//               C: S(u+1) = Q K^T and dP(u+1) = dO V^T on the matrix cores (into the other of two
+//                  register sets), interleaved with P(u) = exp2(S scale log2 e - LSE log2 e),
+//                  dS(u) = P (dP - D) and their packing to bf16 for the first half of the queries;
+//               B: dV^T += dO^T P(u), dK^T += Q^T dS(u) (dO^T, Q^T through transposing LDS reads),
+//                  first-half queries first, interleaved with P and dS of the second half.
 //             Tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden
 //             scores to -inf first (so P = 0 and dS = 0 there).
 // dQ comes from a query-block-outer kernel of its own (fa_bwd_dq.hip), so that every output row has
@@ -244,42 +245,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       // ---- C: S(u+1), dP(u+1) on the matrix cores || P(u), dS(u) on the VALU, then packed
       const FA_LDS float* lse_t = (const FA_LDS float*)(cur + 2 * QTILE);
       const FA_LDS float* del_t = lse_t + 64;
-      auto group = [&](int g) {  // g = 4 qs + gq: four elements of P and dS
-        const int qs = g >> 2, gq = g & 3;
-        const int qloc = 32 * qs + 8 * gq + 4 * half;
-        const f32x4 lse4 = *(const FA_LDS f32x4*)(lse_t + qloc);
-        const f32x4 del4 = *(const FA_LDS f32x4*)(del_t + qloc);
+      // LSE log2 e and D of the lane's 4 queries in each 8-query group gq of each 32-row half qs
+      f32x4 lse4[QS][4], del4[QS][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * gq + e;
-          const float p = fast_exp2(fmaf(s[P][qs][r], cf, -lse4[e]));
-          s[P][qs][r] = p;
-          dp[P][qs][r] = p * (dp[P][qs][r] - del4[e]);
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          lse4[qs][gq] = *(const FA_LDS f32x4*)(lse_t + 32 * qs + 8 * gq + 4 * half);
+          del4[qs][gq] = *(const FA_LDS f32x4*)(del_t + 32 * qs + 8 * gq + 4 * half);
+        }
+      // work unit e of k-step ks (16 queries; e < 4: two elements of P and dS, e = 4: the packing)
+      auto unit = [&](int ks, int e) {
+        const int qs = ks >> 1;
+        if (e < 4) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r = 8 * (ks & 1) + 2 * e + h;
+            const float p = fast_exp2(fmaf(s[P][qs][r], cf, -lse4[qs][r >> 2][r & 3]));
+            s[P][qs][r] = p;
+            dp[P][qs][r] = p * (dp[P][qs][r] - del4[qs][r >> 2][r & 3]);
+          }
+        } else {
+          pb[ks] = pack8(s[P][qs], 8 * (ks & 1));
+          db[ks] = pack8(dp[P][qs], 8 * (ks & 1));
         }
       };
-      auto pack = [&](int ks) {  // one 16-query k-step of P and dS
-        pb[ks] = pack8(s[P][ks >> 1], 8 * (ks & 1));
-        db[ks] = pack8(dp[P][ks >> 1], 8 * (ks & 1));
-      };
-      // VALU items in order: 4 QS groups, then 2 QS packs, spread over the DS k-steps of the scores
-      constexpr int ITEMS = 6 * QS;
-      constexpr int PER = (ITEMS + DS - 1) / DS;
-      auto valu = [&](int ds) {
+      // The VALU work in query order, 5 units per k-step: the first half of the queries beside the
+      // score MFMAs of tile u+1, the second half beside the dV/dK MFMAs of the first half (which do
+      // not need it), each spread evenly, so both matrix-core phases carry VALU work.
+      constexpr int HALF = 5 * QS;  // units per half
+      auto spread = [&](int base, int step, int steps) {  // the units of this step of a phase
 #pragma unroll
-        for (int x = 0; x < PER; ++x) {
-          const int it = ds * PER + x;
-          if (it < 4 * QS) group(it);
-          else if (it < ITEMS) pack(it - 4 * QS);
-        }
+        for (int x = 0; x < HALF; ++x)
+          if (x * steps / HALF == step) unit(base + x / 5, x % 5);
       };
+      auto valu_c = [&](int ds) { spread(0, ds, DS); };
       // (after the last tile the product reads a stale or unwritten stage; its result is unused)
-      scores(std::integral_constant<int, 1 - P>{}, nxt, valu);
+      scores(std::integral_constant<int, 1 - P>{}, nxt, valu_c);
 
-      // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read)
-      constexpr int BS = DT * 2 * QS;  // steps (dt, ks) of 2 MFMAs
+      // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read), k-steps
+      // of queries outermost
+      constexpr int BS = DT * 2 * QS;  // steps (ks, dt) of 2 MFMAs
       bf16x8 bd[3], bq[3];
       auto rdb = [&](int i, bf16x8& d, bf16x8& q) {
-        const int dt = i / (2 * QS), ks = i % (2 * QS);
+        const int ks = i / DT, dt = i % DT;
         const uint32_t tb0 = tile_off<D>(trow, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)) + ks * 16 * D * 2;
         const uint32_t tb8 = tile_off<D>(trow + 8, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)) + ks * 16 * D * 2;
         d = cat(lds_read_tr(cur + QTILE, tb0), lds_read_tr(cur + QTILE, tb8));
@@ -291,9 +300,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       for (int i = 0; i < BS; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (i + 2 < BS) rdb(i + 2, bd[(i + 2) % 3], bq[(i + 2) % 3]);
-        const int dt = i / (2 * QS), ks = i % (2 * QS);
+        const int ks = i / DT, dt = i % DT;
         dvt[dt] = mfma32x32x16(bd[i % 3], pb[ks], dvt[dt]);
         dkt[dt] = mfma32x32x16(bq[i % 3], db[ks], dkt[dt]);
+        if (i < DT * QS) spread(QS, i, DT * QS);
       }
       __builtin_amdgcn_sched_barrier(0);
     };

@@ -21,19 +21,28 @@
 //   * tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden scores to
 //     -inf first; workgroups are ordered heaviest first and, when B*H is a multiple of 8, all
 //     query blocks of one head go to one XCD.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kDqWaves = 4;
+#ifndef FA_DQ_WAVES
+#define FA_DQ_WAVES 8
+#endif
+// 8 waves (two per SIMD) share each K/V tile and a three-stage LDS ring (96 KiB, one workgroup per
+// compute unit), so tiles are fetched two steps ahead; 4 waves use two stages and two workgroups
+// per compute unit.
+constexpr int kDqWaves = FA_DQ_WAVES;
+constexpr int kDqStages = kDqWaves == 8 ? 3 : 2;
 constexpr int kDqRowsPerWave = 32;
-constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // 128 query rows per workgroup
+constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // query rows per workgroup
 constexpr int kDqBc = 64;                         // keys per tile
 
 template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         const float* __restrict__ LSE2,
                                                         const float* __restrict__ DELTA, __bf16* __restrict__ dQ,
@@ -41,17 +50,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict
                                                         const int32_t* __restrict__ seqlens, int nqb, int BH) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kDqBc * D * 2;      // bytes of one K or V tile
-  constexpr int LOADS = kDqBc * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int LOADS = kDqBc * CH / (64 * kDqWaves);  // 16-byte loads per thread per tile
   constexpr int DS = D / 16;               // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;               // 32-wide d tiles of dQ^T
+  // Separate, statically referenced stages (K and V of tile t in stage t % kDqStages)
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf2_raw[kDqStages > 2 ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) char vbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
-  FA_LDS char* kbuf0 = (FA_LDS char*)kbuf0_raw;
-  FA_LDS char* kbuf1 = (FA_LDS char*)kbuf1_raw;
-  FA_LDS char* vbuf0 = (FA_LDS char*)vbuf0_raw;
-  FA_LDS char* vbuf1 = (FA_LDS char*)vbuf1_raw;
+  __shared__ __attribute__((aligned(1024))) char vbuf2_raw[kDqStages > 2 ? TILE : 16];
+  FA_LDS char* const kst[3] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw, (FA_LDS char*)kbuf2_raw};
+  FA_LDS char* const vst[3] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw, (FA_LDS char*)vbuf2_raw};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -199,29 +209,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const __bf16* __restrict
     half_tile(t, 1, kb, vb);
   };
 
-  if (ntiles > 0) {
-    load_tile(Kh, 0, kbuf0);
-    load_tile(Vh, 0, vbuf0);
-  }
-  // tile t in buffers t%2; the load of tile t+1 goes into the other pair, read last in iteration t-1
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_vmem();
+  // Step t: tile t (stage t % NS) must have landed; the next NS - 2 tiles may still be in flight.
+  // After the barrier every wave is done with tile t-1, whose stage receives tile t + NS - 1.
+  constexpr int NS = kDqStages;
+  auto step = [&](auto stage, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    if (NS > 2 && t + 1 < ntiles) wait_vmem_n<(NS - 2) * 2 * LOADS>();
+    else wait_vmem();
     barrier();
-    if (t + 1 < ntiles) {
-      load_tile(Kh, t + 1, kbuf1);
-      load_tile(Vh, t + 1, vbuf1);
+    if (t + NS - 1 < ntiles) {
+      load_tile(Kh, t + NS - 1, kst[(S + NS - 1) % NS]);
+      load_tile(Vh, t + NS - 1, vst[(S + NS - 1) % NS]);
     }
-    if (t < n_wave) tile(t, kbuf0, vbuf0);
-    if (t + 1 < ntiles) {
-      wait_vmem();
-      barrier();
-      if (t + 2 < ntiles) {
-        load_tile(Kh, t + 2, kbuf0);
-        load_tile(Vh, t + 2, vbuf0);
-      }
-      if (t + 1 < n_wave) tile(t + 1, kbuf1, vbuf1);
+    if (t < n_wave) tile(t, kst[S], vst[S]);
+  };
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < ntiles) {
+      load_tile(Kh, i, kst[i]);
+      load_tile(Vh, i, vst[i]);
     }
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2 % NS>;
+  int t = 0;
+  for (; t + NS - 1 < ntiles; t += NS) {
+    step(S0{}, t);
+    step(S1{}, t + 1);
+    if constexpr (NS > 2) step(S2{}, t + 2);
   }
+  if (t < ntiles) step(S0{}, t);
+  if (NS > 2 && t + 1 < ntiles) step(S1{}, t + 1);
 
   // ---- epilogue: dQ = scale acc (bf16, RNE); lane holds query `query`, d = 32 dt + 8 gq + 4 half + 0..3
   if (query < N) {
@@ -242,7 +260,7 @@ hipError_t launch(const Problem& p, const void* q, const void* k, const void* v,
                   const float* delta, void* dq) {
   const int nqb = (p.N + kDqBr - 1) / kDqBr;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)(nqb * BH)), dim3(kDqWaves * 64), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta, (__bf16*)dq,
                      p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, nqb, BH);
   return hipGetLastError();
