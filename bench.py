@@ -1,6 +1,9 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload 4] [--no-cpu-baseline]
+                    [--cold]
+    python bench.py --all-configs      (every workload, its fraction of the per-config roofline)
+    python bench.py --naive-torch      (the materialising attention as plain torch ops; context)
 
 One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_dkdv,
 fa_backward_dq -- exactly what fa_backward runs) over one batch of the synthetic workload,
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal, N=4096 d=128) and % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_VALU_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on the VALU)
 
 
 def visible_pairs(N: int, causal: bool, key_len: int) -> int:
@@ -102,9 +106,126 @@ def cpu_baseline(w, x, target_s: float = 12.0):
     t = run(nh) if nh > 1 else t1
     L = w.N if sl is None else int(sl[0])
     flops = 4.0 * w.d * visible_pairs(w.N, w.causal, L) * nh * 3.5
+    # the oracle itself is dense: it materialises every (query, key) pair, forward 4 N^2 d, and its
+    # backward 8 N^2 d (it keeps P)
+    oracle_flops = 12.0 * w.N * w.N * w.d * nh
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpoolctl.threadpool_info()]
+    except Exception:
+        pass
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"fp64 oracle forward+backward of the first {nh} of the {w.B * w.H} (batch, head) pairs, "
-                      f"{t:.1f} s wall; algorithmic FLOPs as for the GPU"}
+                      f"{t:.1f} s wall; algorithmic FLOPs as for the GPU",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model, "blas": blas,
+            "oracle_flops": oracle_flops, "oracle_gflops_per_s": round(oracle_flops / t / 1e9, 2)}
+
+
+def min_bytes(w):
+    """Algorithmic HBM bytes: forward (3 reads + 1 write of [B,H,N,d] + LSE), backward (5 reads +
+    3 writes + 12 B of row statistics per row)."""
+    es = 2 if w.dtype == "bf16" else 4
+    t = w.B * w.H * w.N * w.d * es
+    rows = w.B * w.H * w.N
+    return 4 * t + 4 * rows, 8 * t + 12 * rows
+
+
+def naive_torch_forward(w, x, steps: int):
+    """The materialising attention (S written, softmax, P V) as plain torch ops, timed on the GPU:
+    context for the fused kernels, never a fallback."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kt = k.transpose(-1, -2).contiguous()
+    mask = None
+    if w.causal:
+        mask = torch.ones(w.N, w.N, dtype=torch.bool, device=dev).triu(1)
+
+    def fwd():
+        s = torch.matmul(q, kt) * x["scale"]
+        if mask is not None:
+            s = s.masked_fill(mask, float("-inf"))
+        p = torch.softmax(s.float(), dim=-1).to(q.dtype)
+        return torch.matmul(p, v)
+
+    for _ in range(3):
+        fwd()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fwd()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = False):
+    """Time `steps` fwd+bwd steps of workload w (inputs resident on the device): clock settling,
+    warm-up, then HIP events around the timed region and around every launch."""
+    import statistics
+
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    sl = None if x["seqlens"] is None else x["seqlens"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    scale, causal = x["scale"], w.causal
+    flops_fwd, flops_bwd, flops_dkdv, flops_dq = workload_flops(w, x)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
+        if e: e[1].record(stream)
+        fa.fa_backward_prepare(o, do, lse, ws)
+        if e: e[2].record(stream)
+        fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale, causal, sl, ws)
+        if e: e[3].record(stream)
+        fa.fa_backward_dq(q, k, v, do, lse, dq, scale, causal, sl, ws)
+        if e: e[4].record(stream)
+
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        step(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    names = ("fwd", "pre", "dkdv", "dq")
+    per = {n: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, n in enumerate(names)}
+    r = {"ms_step": t_start.elapsed_time(t_end) / steps, "flops_fwd": flops_fwd, "flops_bwd": flops_bwd,
+         "flops_dkdv": flops_dkdv, "flops_dq": flops_dq,
+         "med": {n: round(statistics.median(v), 4) for n, v in per.items()},
+         "min": {n: round(min(v), 4) for n, v in per.items()}}
+    for n in names:
+        r["ms_" + n] = sum(per[n]) / steps
+    r["ms_bwd"] = r["ms_pre"] + r["ms_dkdv"] + r["ms_dq"]
+    return r
 
 
 def main():
@@ -116,6 +237,12 @@ def main():
                     help="repeat the step untimed for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps with a 512 MiB scratch write between them (cold caches)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="only time every workload and print one line each with its per-config roofline fraction")
+    ap.add_argument("--naive-torch", action="store_true",
+                    help="only time the materialising attention forward as plain torch ops (context)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), to scale the HBM "
                          "byte counters of a profiler run, and exit")
@@ -142,54 +269,44 @@ def main():
     import workloads
 
     fa.load()
+    if args.all_configs:
+        for wid in sorted(workloads.WORKLOADS):
+            w = workloads.WORKLOADS[wid]
+            x = workloads.draw(w)
+            r = measure(fa, w, x, max(3, args.steps // 4), 2, args.settle_ms)
+            fb, bb = min_bytes(w)
+            ff, fbw = r["flops_fwd"], r["flops_bwd"]
+            peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_VALU_TFLOPS
+            roof_f = min(peak, ff / fb * PEAK_HBM_GBS / 1e3)
+            roof_b = min(peak, fbw / bb * PEAK_HBM_GBS / 1e3)
+            tf = ff / (r["ms_fwd"] * 1e-3) / 1e12
+            tb = fbw / (r["ms_bwd"] * 1e-3) / 1e12
+            print(json.dumps({"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
+                              "causal": w.causal, "key_padding": w.padded,
+                              "fwd_ms": round(r["ms_fwd"], 4), "fwd_tflops": round(tf, 2),
+                              "fwd_ai_flop_per_byte": round(ff / fb, 1), "fwd_roofline_tflops": round(roof_f, 1),
+                              "fwd_frac_of_roofline": round(tf / roof_f, 4),
+                              "bwd_ms": round(r["ms_bwd"], 4), "bwd_tflops": round(tb, 2),
+                              "bwd_ai_flop_per_byte": round(fbw / bb, 1), "bwd_roofline_tflops": round(roof_b, 1),
+                              "bwd_frac_of_roofline": round(tb / roof_b, 4)}), flush=True)
+        return
+
     w = workloads.WORKLOADS[args.workload]
     x = workloads.draw(w)
-    dev = torch.device("cuda:0")
-    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
-    sl = None if x["seqlens"] is None else x["seqlens"].to(dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
-    scale, causal = x["scale"], w.causal
-    flops_fwd, flops_bwd, flops_dkdv, flops_dq = workload_flops(w, x)
-
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-
-    def step(e=None):
-        if e: e[0].record(stream)
-        fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
-        if e: e[1].record(stream)
-        fa.fa_backward_prepare(o, do, lse, ws)
-        if e: e[2].record(stream)
-        fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale, causal, sl, ws)
-        if e: e[3].record(stream)
-        fa.fa_backward_dq(q, k, v, do, lse, dq, scale, causal, sl, ws)
-        if e: e[4].record(stream)
-
-    t_settle = time.perf_counter()
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(ev[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-
-    def avg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in ev) / args.steps
-
-    ms_fwd, ms_pre, ms_dkdv, ms_dq = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
-    ms_bwd = ms_pre + ms_dkdv + ms_dq
+    if args.naive_torch:
+        ms = naive_torch_forward(w, x, args.steps)
+        ff = workload_flops(w, x)[0]
+        es = 2 if w.dtype == "bf16" else 4
+        print(json.dumps({"workload": w.name, "naive_torch_fwd_ms": round(ms, 4),
+                          "naive_torch_fwd_tflops": round(ff / (ms * 1e-3) / 1e12, 2),
+                          "materialised_score_bytes": w.B * w.H * w.N * w.N * es,
+                          "note": "S = q k^T scale, masked_fill, softmax in fp32, P V: plain torch ops; context only"}),
+              flush=True)
+        return
+    r = measure(fa, w, x, args.steps, args.warmup, args.settle_ms)
+    ms_step, ms_fwd, ms_pre, ms_dkdv, ms_dq = r["ms_step"], r["ms_fwd"], r["ms_pre"], r["ms_dkdv"], r["ms_dq"]
+    ms_bwd = r["ms_bwd"]
+    flops_fwd, flops_bwd, flops_dkdv, flops_dq = r["flops_fwd"], r["flops_bwd"], r["flops_dkdv"], r["flops_dq"]
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
     kernels = {"fwd_bf16_kernel": (ms_fwd, flops_fwd), "bwd_dkdv_kernel": (ms_dkdv, flops_dkdv),
                "bwd_dq_kernel": (ms_dq, flops_dq)}
@@ -203,16 +320,23 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "key_padding": w.padded, "q_std": w.q_std, "parallelism": "single GPU"},
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+        "fwd": {"ms": round(ms_fwd, 4), "ms_median": r["med"]["fwd"], "ms_min": r["min"]["fwd"],
+                "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
                 "pct_of_mfma_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(ms_bwd, 4), "ms_prepare": round(ms_pre, 4), "ms_dkdv": round(ms_dkdv, 4),
-                "ms_dq": round(ms_dq, 4), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
+                "ms_dq": round(ms_dq, 4), "ms_median": {k: r["med"][k] for k in ("pre", "dkdv", "dq")},
+                "ms_min": {k: r["min"][k] for k in ("pre", "dkdv", "dq")},
+                "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
         "flops": {"fwd": flops_fwd, "bwd": flops_bwd},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                      "ms_per_launch": round(dom_ms, 4)},
     }
+    if args.cold:
+        rc = measure(fa, w, x, args.steps, args.warmup, 0.0, cold=True)
+        out["cold"] = {"note": "512 MiB scratch written between steps (outside the timed kernels)",
+                       "ms_fwd": round(rc["ms_fwd"], 4), "ms_bwd": round(rc["ms_bwd"], 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)

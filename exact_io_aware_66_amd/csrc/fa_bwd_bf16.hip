@@ -36,6 +36,10 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerWave = 32;
 constexpr int kBwdBc = kBwdWaves * kBwdKeysPerWave;  // 128 keys per workgroup
+#ifndef FA_BWD_READ_AHEAD
+#define FA_BWD_READ_AHEAD 2
+#endif
+constexpr int kRA = FA_BWD_READ_AHEAD;  // LDS operand fragments read this many MFMA steps ahead
 
 // ---------------------------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic and (bf16 path) LSE_i log2(e).  D/8 threads per row.
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     // `between(ds)` places other work after the MFMAs of k-step ds.
     auto scores = [&](auto par, const FA_LDS char* st, auto&& between) __attribute__((always_inline)) {
       constexpr int P = decltype(par)::value;
-      bf16x8 fq[3][QS], fd[3][QS];
+      bf16x8 fq[kRA + 1][QS], fd[kRA + 1][QS];
       auto rd = [&](int ds, bf16x8 (&q)[QS], bf16x8 (&d)[QS]) {
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
@@ -198,16 +202,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         s[P][qs] = zero16();
         dp[P][qs] = zero16();
       }
-      rd(0, fq[0], fd[0]);
-      if (DS > 1) rd(1, fq[1], fd[1]);
+#pragma unroll
+      for (int ds = 0; ds < kRA && ds < DS; ++ds) rd(ds, fq[ds], fd[ds]);
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         __builtin_amdgcn_sched_barrier(0);
-        if (ds + 2 < DS) rd(ds + 2, fq[(ds + 2) % 3], fd[(ds + 2) % 3]);
+        if (ds + kRA < DS) rd(ds + kRA, fq[(ds + kRA) % (kRA + 1)], fd[(ds + kRA) % (kRA + 1)]);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
-          s[P][qs] = mfma32x32x16(fq[ds % 3][qs], kb[ds], s[P][qs]);
-          dp[P][qs] = mfma32x32x16(fd[ds % 3][qs], vb[ds], dp[P][qs]);
+          s[P][qs] = mfma32x32x16(fq[ds % (kRA + 1)][qs], kb[ds], s[P][qs]);
+          dp[P][qs] = mfma32x32x16(fd[ds % (kRA + 1)][qs], vb[ds], dp[P][qs]);
         }
         between(ds);
       }
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read), k-steps
       // of queries outermost
       constexpr int BS = DT * 2 * QS;  // steps (ks, dt) of 2 MFMAs
-      bf16x8 bd[3], bq[3];
+      bf16x8 bd[kRA + 1], bq[kRA + 1];
       auto rdb = [&](int i, bf16x8& d, bf16x8& q) {
         const int ks = i / DT, dt = i % DT;
         const uint32_t tb0 = tile_off<D>(trow, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)) + ks * 16 * D * 2;
@@ -294,15 +298,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         d = cat(lds_read_tr(cur + QTILE, tb0), lds_read_tr(cur + QTILE, tb8));
         q = cat(lds_read_tr(cur, tb0), lds_read_tr(cur, tb8));
       };
-      rdb(0, bd[0], bq[0]);
-      rdb(1, bd[1], bq[1]);
+#pragma unroll
+      for (int i = 0; i < kRA && i < BS; ++i) rdb(i, bd[i], bq[i]);
 #pragma unroll
       for (int i = 0; i < BS; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i + 2 < BS) rdb(i + 2, bd[(i + 2) % 3], bq[(i + 2) % 3]);
+        if (i + kRA < BS) rdb(i + kRA, bd[(i + kRA) % (kRA + 1)], bq[(i + kRA) % (kRA + 1)]);
         const int ks = i / DT, dt = i % DT;
-        dvt[dt] = mfma32x32x16(bd[i % 3], pb[ks], dvt[dt]);
-        dkt[dt] = mfma32x32x16(bq[i % 3], db[ks], dkt[dt]);
+        dvt[dt] = mfma32x32x16(bd[i % (kRA + 1)], pb[ks], dvt[dt]);
+        dkt[dt] = mfma32x32x16(bq[i % (kRA + 1)], db[ks], dkt[dt]);
         if (i < DT * QS) spread(QS, i, DT * QS);
       }
       __builtin_amdgcn_sched_barrier(0);

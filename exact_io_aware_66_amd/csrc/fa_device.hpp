@@ -137,9 +137,13 @@ __device__ __forceinline__ void gload_lds4(const void* gptr, FA_LDS void* lds_ba
 // A buffer load whose per-lane byte offset is >= bytes returns zeros instead of touching memory, so
 // rows past the end of a tensor need neither a clamp nor a branch.  The fourth word is the
 // gfx9-family raw-buffer format.
+// (The fields go through readfirstlane, as does the LDS base of the loads below: they are
+// wave-uniform, and the inline assembly that uses them requires scalar registers.)
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)max(bytes, 0), 0x00020000u};
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(max(bytes, 0)), 0x00020000u};
 }
 // 16 bytes at byte offset voff of the buffer straight into LDS at (wave-uniform) lds_base + 16 * lane
 // (buffer_load_dwordx4 ... lds, LDS base in M0).  Issued through inline assembly so that the
@@ -151,14 +155,14 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
 __device__ __forceinline__ void bload_lds16(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(r), "s"((uint32_t)(uintptr_t)lds_base)
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base))
                : "memory", "m0");
 }
 // 4 bytes at byte offset voff of the buffer into LDS at (wave-uniform) lds_base + 4 * lane.
 __device__ __forceinline__ void bload_lds4(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(r), "s"((uint32_t)(uintptr_t)lds_base)
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
