@@ -39,7 +39,13 @@ constexpr int kBwdBc = kBwdWaves * kBwdKeysPerWave;  // 128 keys per workgroup
 #ifndef FA_BWD_READ_AHEAD
 #define FA_BWD_READ_AHEAD 2
 #endif
-constexpr int kRA = FA_BWD_READ_AHEAD;  // LDS operand fragments read this many MFMA steps ahead
+#ifndef FA_BWD_READ_AHEAD_B
+#define FA_BWD_READ_AHEAD_B 2
+#endif
+// LDS operand fragments are read this many MFMA steps ahead: row reads (score phase) and
+// transposing reads (dV/dK phase)
+constexpr int kRA = FA_BWD_READ_AHEAD;
+constexpr int kRB = FA_BWD_READ_AHEAD_B;
 
 // ---------------------------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic and (bf16 path) LSE_i log2(e).  D/8 threads per row.
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read), k-steps
       // of queries outermost
       constexpr int BS = DT * 2 * QS;  // steps (ks, dt) of 2 MFMAs
-      bf16x8 bd[kRA + 1], bq[kRA + 1];
+      bf16x8 bd[kRB + 1], bq[kRB + 1];
       auto rdb = [&](int i, bf16x8& d, bf16x8& q) {
         const int ks = i / DT, dt = i % DT;
         const uint32_t tb0 = tile_off<D>(trow, 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)) + ks * 16 * D * 2;
@@ -299,14 +305,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         q = cat(lds_read_tr(cur, tb0), lds_read_tr(cur, tb8));
       };
 #pragma unroll
-      for (int i = 0; i < kRA && i < BS; ++i) rdb(i, bd[i], bq[i]);
+      for (int i = 0; i < kRB && i < BS; ++i) rdb(i, bd[i], bq[i]);
 #pragma unroll
       for (int i = 0; i < BS; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kRA < BS) rdb(i + kRA, bd[(i + kRA) % (kRA + 1)], bq[(i + kRA) % (kRA + 1)]);
+        if (i + kRB < BS) rdb(i + kRB, bd[(i + kRB) % (kRB + 1)], bq[(i + kRB) % (kRB + 1)]);
         const int ks = i / DT, dt = i % DT;
-        dvt[dt] = mfma32x32x16(bd[i % (kRA + 1)], pb[ks], dvt[dt]);
-        dkt[dt] = mfma32x32x16(bq[i % (kRA + 1)], db[ks], dkt[dt]);
+        dvt[dt] = mfma32x32x16(bd[i % (kRB + 1)], pb[ks], dvt[dt]);
+        dkt[dt] = mfma32x32x16(bq[i % (kRB + 1)], db[ks], dkt[dt]);
         if (i < DT * QS) spread(QS, i, DT * QS);
       }
       __builtin_amdgcn_sched_barrier(0);

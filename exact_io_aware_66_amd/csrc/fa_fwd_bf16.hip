@@ -12,22 +12,24 @@
 // tile is set by the register file, LDS and issue model of a CDNA4 compute unit):
 //   * one workgroup = 4 waves of one (batch, head), one wave per SIMD; a wave owns 32 query rows
 //     (128 per workgroup), fits in 256 registers, and two workgroups share a compute unit so each
-//     covers the other's memory and barrier stalls (64 rows per wave is a compile-time option);
+//     covers the other's memory and barrier stalls;
 //   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16);
 //     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
 //     lane halves hold different keys of the same queries and are combined once, at the end);
 //   * K and V tiles of 64 keys stream through two double-buffered LDS rings with direct
-//     buffer->LDS 16-byte loads (rows past N read as zeros); K runs one tile ahead of V, so each load has a full iteration to
-//     land before it is read;
-//   * software pipeline: S(t+1) = K(t+1) Q^T is issued on the matrix cores while the VALU turns
-//     S(t) into P(t) (exp2, bf16 pack, row sums) and O^T += V(t-1)^T P(t-1)^T runs beside it; the
-//     instruction streams are interleaved by explicit schedule groups, LDS fragments are read two
-//     MFMA steps ahead, and V^T is read through ds_read_b64_tr_b16;
+//     buffer->LDS 16-byte loads (rows past N read as zeros), one tile ahead;
+//   * software pipeline, iteration t (scores of consecutive tiles alternate between two register
+//     sets):  S(t+1) = K(t+1) Q^T on the matrix cores while the VALU turns S(t) into P(t) (exp2,
+//     bf16 pack, row sums); then O^T += V(t)^T P(t)^T, beside which the VALU finishes P(t) and
+//     checks S(t+1) against the running maximum.  Each matrix-core step carries its share of the
+//     VALU work, and LDS fragments are read two MFMA steps ahead (V^T through ds_read_b64_tr_b16);
 //   * lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by more
 //     than 2^8 (base 2), so p <= 2^8 and the output/normaliser, which share the stale maximum, stay
-//     exact; the O rescale (128 accumulator registers) therefore runs a few times per row instead of
-//     once per tile.  Normalisation by l is deferred to the epilogue;
-//   * masked tiles (causal diagonal, key padding, ragged tail) take a separate exact path;
+//     exact; the O rescale therefore runs a few times per row instead of once per tile.  The check
+//     for tile t+1 overlaps the P(t) V(t) products, so it is off the critical path.  Normalisation
+//     by l is deferred to the epilogue;
+//   * tiles with hidden pairs (causal diagonal, key padding, ragged tail) are masked, with an exact
+//     maximum update, in a separate form of the iteration;
 //   * workgroups are ordered heaviest first (causal) and, when B*H is a multiple of 8, all query
 //     blocks of one head go to one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so a
 //     head's K/V stays in that XCD's L2.
@@ -40,16 +42,13 @@ namespace fa {
 namespace {
 
 constexpr int kFwdWaves = 4;
-// Query rows per wave.  32: a wave fits in 256 registers and two workgroups share a compute unit,
-// each covering the other's memory and barrier stalls.  64: one workgroup per compute unit, and
-// every K/V fragment read from LDS feeds twice as many rows.
-constexpr int kFwdRowsPerWave = FA_FWD_ROWS_PER_WAVE;
-constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // query rows per workgroup
+constexpr int kFwdRowsPerWave = 32;                  // query rows per wave (one 32-column MFMA tile)
+constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 128 query rows per workgroup
 constexpr int kFwdBc = 64;                           // keys per tile
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
 template <int D, bool CAUSAL, bool PADDED, bool NEG>
-__global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens, int nqb, int BH) {
@@ -58,20 +57,14 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
   constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
   constexpr int DS = D / 16;                // k-steps of S = K Q^T
   constexpr int DT = D / 32;                // 32-wide d tiles of O^T
-  constexpr int QT = kFwdRowsPerWave / 32;  // 32-row query halves of a wave
-  constexpr bool QLDS = D == 128 && QT == 2;  // Q fragments from LDS instead of registers
-  constexpr int VALU3 = QT * 4 * 24;        // VALU instructions of P(t): 4 QT groups x (8 fma, 8 exp, 4 cvt, 4 dot)
-  // Separate LDS arrays, each referenced statically, so the compiler sees that a direct load into
-  // one buffer never aliases the reads of another.
+  // Separate LDS arrays, each referenced statically, so that the compiler sees which buffer every
+  // read addresses.
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
-  __shared__ __attribute__((aligned(1024))) char qbuf_raw[QLDS ? kFwdWaves * kFwdRowsPerWave * D * 2 : 16];
-  FA_LDS char* kbuf0 = (FA_LDS char*)kbuf0_raw;
-  FA_LDS char* kbuf1 = (FA_LDS char*)kbuf1_raw;
-  FA_LDS char* vbuf0 = (FA_LDS char*)vbuf0_raw;
-  FA_LDS char* vbuf1 = (FA_LDS char*)vbuf1_raw;
+  FA_LDS char* const kbuf[2] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw};
+  FA_LDS char* const vbuf[2] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -100,54 +93,33 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
   const int L = PADDED ? clamp_len(seqlens, b, N) : N;  // keys >= L are invisible
   const int q0 = qblock * kFwdBr;
   const int qw = q0 + wave * kFwdRowsPerWave;
+  const int query = qw + l32;
   const int kv_end = CAUSAL ? min(L, q0 + kFwdBr) : L;
   const int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;  // tiles the workgroup loads
   const int wave_end = CAUSAL ? min(L, qw + kFwdRowsPerWave) : L;
-  const int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes
+  const int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes (>= 1 when L > 0)
   int n_full = L / kFwdBc;                              // leading tiles with no hidden pair
   if (CAUSAL) n_full = min(n_full, qw / kFwdBc);
+  const int n_clean = min(n_full, n_wave);
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane holds query qw + 32 qt + l32, d = 16 ds + 8 half
-  // .. +7.  d=64: kept in registers.  d=128: the wave's 64 rows are staged once in its own LDS
-  // region (16 KiB) and the fragments are read per k-step, which keeps the wave within 256 VGPRs.
-  bf16x8 qf[QT][QLDS ? 1 : DS];
-  FA_LDS char* qbuf = (FA_LDS char*)qbuf_raw + wave * (QLDS ? kFwdRowsPerWave * D * 2 : 0);
-  if constexpr (QLDS) {
-    const u32x4 rq = make_rsrc(Qh + (int64_t)qw * D, (N - qw) * D * 2);  // rows past N read as zeros
+  // Q^T fragments (B operand of S^T = K Q^T): lane holds query `query`, d = 16 ds + 8 half .. +7
+  bf16x8 qf[DS];
 #pragma unroll
-    for (int n = 0; n < kFwdRowsPerWave * CH / 64; ++n) {
-      const int p = n * 64 + lane;
-      const int r = p / CH;
-      const int c = (p % CH) ^ swz<D>(r);
-      bload_lds16(rq, (uint32_t)(r * D + 8 * c) * 2, qbuf + n * 1024);
-    }
-  } else {
+  for (int ds = 0; ds < DS; ++ds) {
+    if (query < N) {
+      qf[ds] = *(const bf16x8*)(Qh + (int64_t)query * D + 16 * ds + 8 * half);
+    } else {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int row = qw + 32 * qt + l32;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        if (row < N) {
-          qf[qt][ds] = *(const bf16x8*)(Qh + (int64_t)row * D + 16 * ds + 8 * half);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qf[qt][ds][e] = (__bf16)0.f;
-        }
-      }
+      for (int e = 0; e < 8; ++e) qf[ds][e] = (__bf16)0.f;
     }
   }
 
-  f32x16 acc[QT][DT];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = zero16();
-  float m_run[QT], l_run[QT];  // base-2 running maximum (identical in both lane halves); per-lane
-#pragma unroll                 // partial normaliser (this lane's keys)
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+  // Base-2 running maximum (identical in both lane halves), the maximum P is taken against (0 while
+  // the row has seen no visible key), and the per-lane partial normaliser (this lane's keys).
+  float m_run = -INFINITY, m_p = 0.f, l_run = 0.f;
 
   // K/V tile loads: buffer loads straight into LDS; rows past N read as zeros (the buffer ends at
   // the head's last row; those keys are masked).  K and V tiles share the per-lane byte offsets,
@@ -166,238 +138,284 @@ __global__ __launch_bounds__(256, kFwdRowsPerWave == 32 ? 2 : 1) void fwd_bf16_k
     for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kFwdWaves + wave) * 1024);
   };
 
-  // S^T(tile in kb) = K Q^T, 4 independent accumulators, one K fragment per (ds, kt)
-  auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[2][QT]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = zero16();
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      bf16x8 qd[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        qd[qt] = QLDS ? lds_read_b128(qbuf, tile_off<D>(32 * qt + l32, 16 * ds + 8 * half)) : qf[qt][QLDS ? 0 : ds];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma32x32x16(kf, qd[qt], s[kt][qt]);
-      }
-    }
-    pipe_schedule<DS, QLDS ? 4 : 2, 2 * QT, 0, 2, 1>();  // fragment reads two k-steps ahead of their MFMAs
-  };
-
-  f32x16 s[2][QT];  // S^T(t): s[kt][qt], lane = query column, rows = keys 32 kt + 8 (r/4) + 4 half + r%4
-  bf16x8 pf[QT][4], pn[QT][4];  // P(t-1) (consumed by O += P V) and P(t) (being produced), packed bf16
+  // S^T of two consecutive tiles: s[set][kt], lane = query column, rows = keys 32 kt + 8 (r/4) +
+  // 4 half + r%4 of the tile
+  f32x16 s[2][2];
+  bf16x8 pn[4];  // P(t) packed to bf16 (B operand of O^T += V^T P^T), one per 16-key k-step
+  bf16x2 pk[4][4];
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   const int g = lane >> 4, j = lane & 15;
   const int vrow = 4 * (g >> 1) + (j >> 2);
 
-  // P(t) = exp2(s cf - m) packed to bf16 (the B operand of O^T += V^T P^T), with the row sums taken
-  // by v_dot2_f32_bf16 on the packed values, so the normaliser sums exactly the weights used.
-  auto probs = [&](float cf, const float (&m_use)[QT]) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kt = ks >> 1, base = 8 * (ks & 1);
-        bf16x2 pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x2 two = {fast_exp2(fmaf(s[kt][qt][base + 2 * e], cf, -m_use[qt])),
-                             fast_exp2(fmaf(s[kt][qt][base + 2 * e + 1], cf, -m_use[qt]))};
-          pk[e] = __builtin_convertvector(two, bf16x2);
-          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pk[e], ones, l_run[qt], false);
-        }
-        pn[qt][ks] = cat(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
-                         __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3));
-      }
+  // Work units of the VALU, placed between the MFMAs of the matrix-core phases:
+  //   punit(set, ks, e): two elements of P(t) (k-step ks, pair e) = exp2(s cf - m_p), their bf16
+  //     pack and row sum (v_dot2_f32_bf16 on the packed values, so l sums exactly the weights used);
+  //   xunit(set, u): four scores of the next tile into the running extreme ext (max, or min for a
+  //     negative scale) for the lazy check.
+  auto punit = [&](int set, int ks, int e, float cf) {
+    const int kt = ks >> 1, r = 8 * (ks & 1) + 2 * e;
+    const f32x2 two = {fast_exp2(fmaf(s[set][kt][r], cf, -m_p)), fast_exp2(fmaf(s[set][kt][r + 1], cf, -m_p))};
+    pk[ks][e] = __builtin_convertvector(two, bf16x2);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[ks][e], ones, l_run, false);
+    if (e == 3)
+      pn[ks] = cat(__builtin_shufflevector(pk[ks][0], pk[ks][1], 0, 1, 2, 3),
+                   __builtin_shufflevector(pk[ks][2], pk[ks][3], 0, 1, 2, 3));
+  };
+  float ext = 0.f;
+  auto xunit = [&](int set, int u) {
+    const int kt = u >> 2, r = 4 * (u & 3);
+    const f32x16& v = s[set][kt];
+    if (u == 0) ext = v[0];
+    ext = NEG ? fminf(fminf(ext, v[r]), fminf(v[r + 1], fminf(v[r + 2], v[r + 3])))
+              : fmaxf(fmaxf(ext, v[r]), fmaxf(v[r + 1], fmaxf(v[r + 2], v[r + 3])));
   };
 
-  // O^T += V^T P^T for the tile in vb, over 4 k-steps of 16 keys.  V^T fragment for (dt, ks): lane
-  // (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and 16 ks + 8 + 4 half + 0..3, the key
-  // order of pf; two transposing reads supply them.  Each lane reads from two base addresses (rows
-  // vrow and vrow + 8) plus compile-time offsets of 16 rows.
-  auto pv = [&](const FA_LDS char* vb) {
+  // S^T(tile in kb) = K Q^T into s[set]: DS k-steps of 2 MFMAs, K fragments read two k-steps ahead;
+  // `between(ds)` places VALU work after the MFMAs of k-step ds
+  auto scores = [&](int set, const FA_LDS char* kb, auto&& between) __attribute__((always_inline)) {
+    bf16x8 kf[3][2];
+    auto rd = [&](int ds, bf16x8 (&f)[2]) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      // rows vrow + 16 ks share the swizzle; rows vrow + 8 + 16 ks need their own base
-      const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
-      const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3));
+      for (int kt = 0; kt < 2; ++kt) f[kt] = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
+    };
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 vf = cat(lds_read_tr(vb, off0 + ks * 16 * D * 2), lds_read_tr(vb, off8 + ks * 16 * D * 2));
+    for (int kt = 0; kt < 2; ++kt) s[set][kt] = zero16();
+    rd(0, kf[0]);
+    rd(1, kf[1]);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32x32x16(vf, pf[qt][ks], acc[qt][dt]);
-      }
+    for (int ds = 0; ds < DS; ++ds) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ds + 2 < DS) rd(ds + 2, kf[(ds + 2) % 3]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[set][kt] = mfma32x32x16(kf[ds % 3][kt], qf[ds], s[set][kt]);
+      between(ds);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // O^T += V^T P^T for k-steps [ks0, ks0 + 2) of the tile in vb, k-step outermost: 2 DT MFMAs.  V^T
+  // fragment for (dt, ks): lane (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and
+  // 16 ks + 8 + 4 half + 0..3, the key order of pn; two transposing reads supply them (bases for
+  // rows vrow and vrow + 8, compile-time offsets of 16 rows).  `between(i)` follows MFMA i.
+  auto pv = [&](const FA_LDS char* vb, int ks0, auto&& between) __attribute__((always_inline)) {
+    constexpr int NS = 2 * DT;
+    bf16x8 vf[3];
+    auto rd = [&](int i, bf16x8& f) {
+      const int ks = ks0 + i / DT, dt = i % DT;
+      const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+      const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+      f = cat(lds_read_tr(vb, off0), lds_read_tr(vb, off8));
+    };
+    rd(0, vf[0]);
+    rd(1, vf[1]);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < NS) rd(i + 2, vf[(i + 2) % 3]);
+      const int ks = ks0 + i / DT, dt = i % DT;
+      acc[dt] = mfma32x32x16(vf[i % 3], pn[ks], acc[dt]);
+      between(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Exact update for a tile with hidden pairs (scores in s[set]): hidden scores to -inf, the rest
+  // scaled to the base-2 domain in place; raise the maximum to the tile's.  Returns the factor O and
+  // l must be multiplied by (1 when the maximum is unchanged).
+  auto mask_update = [&](int set, int t) -> float {
+    const int key0 = t * kFwdBc;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = (key < L) & (!CAUSAL | (key <= query));
+        const float v = vis ? s[set][kt][r] * c_log2 : -INFINITY;
+        s[set][kt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_p - m_use);
+    m_run = m_new;
+    m_p = m_use;
+    return alpha;
+  };
+  // Exact maximum of a fully visible tile (the first one of the wave): no rescale needed before it.
+  auto exact_update = [&](int set) -> float {
+    float mx = s[set][0][0];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = NEG ? fminf(mx, s[set][kt][r]) : fmaxf(mx, s[set][kt][r]);
+    mx = (NEG ? min_halves(mx) : max_halves(mx)) * c_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_p - m_new);
+    m_run = m_new;
+    m_p = m_new;
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    l_run *= alpha;
+  };
+
+  // ---- prologue: K(0), K(1), V(0); S(0) and its exact update
   if (ntiles > 0) {
-    load_tile(Kh, 0, kbuf0);
-    if (ntiles > 1) load_tile(Kh, 1, kbuf1);
+    load_tile(Kh, 0, kbuf[0]);
+    if (ntiles > 1) load_tile(Kh, 1, kbuf[1]);
+    load_tile(Vh, 0, vbuf[0]);
   }
-  // The first iteration adds P(-1) V(-1) with P(-1) = 0 from a zeroed buffer: an exact no-op that
-  // keeps a single (interleaved) code path for every iteration.
-  for (int i = threadIdx.x; i < TILE / 16; i += 256) *(FA_LDS u32x4*)(vbuf1 + 16 * i) = u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[qt][ks][e] = (__bf16)0.f;
   wait_vmem();
-  __syncthreads();
-  if (n_wave > 0) scores(kbuf0, s);
+  barrier();
+  if (n_wave > 0) {
+    scores(0, kbuf[0], [](int) {});
+    if (n_clean > 0) exact_update(0);
+    else mask_update(0, 0);
+  }
 
-  // Iteration t (0 <= t <= ntiles): S(t) is in s and P(t-1) in pf.  kn holds K(t+1), vp holds V(t-1);
-  // K(t+2) is loaded into kl and V(t) into vl (both last read in iteration t-1).  Every wave runs
-  // all ntiles + 1 iterations (one barrier each) in one of four forms, chosen outside the loop so
-  // that each form is straight-line code (a data-dependent branch around in-place updates of the
-  // score registers makes the compiler copy them on every iteration):
-  //   kClean  (t < n_clean):           lazy maximum check; [O += P(t-1) V(t-1) || P(t)]; S(t+1)
-  //   kMasked (n_clean <= t < n_wave): mask + exact maximum update; the same products
-  //   kDrain  (t == n_wave):           O += P(t-1) V(t-1) only
-  //   kIdle   (t > n_wave):            only the workgroup's loads
-  // (S(t+1) is computed even when no tile t+1 follows; it is then unused.)
-  constexpr int kClean = 0, kMasked = 1, kDrain = 2, kIdle = 3;
-  auto step = [&](auto mode, int t, const FA_LDS char* kn, FA_LDS char* kl, const FA_LDS char* vp, FA_LDS char* vl)
-      __attribute__((always_inline)) {
-    constexpr int MODE = decltype(mode)::value;
-    wait_vmem();  // K(t+1) and V(t-1), issued one iteration ago, have landed
+  // Iteration t (every wave runs t = 0 .. ntiles-1, one barrier each; V(t) and K(t+1) were loaded
+  // one iteration ahead).  S(t) is in s[t % 2] (scaled and masked in place when tile t has hidden
+  // pairs, else raw: cf tells which), and the maximum for P(t) is settled.
+  //   phase 1:  S(t+1) = K(t+1) Q^T into the other set  ||  P(t), k-steps 0..2
+  //   phase 2a: O += V(t)^T P(t), k-steps 0, 1           ||  P(t), k-step 3; extreme of S(t+1), first half
+  //   phase 2b: O += V(t)^T P(t), k-steps 2, 3           ||  extreme of S(t+1), second half
+  //   then the lazy check for tile t+1 (raise the maximum, rescale O and l), or, when tile t+1 has
+  //   hidden pairs, its mask and exact update.
+  // The forms differ in the next tile (fully visible, with hidden pairs, none) and in whether the
+  // set and buffer indices are compile-time (the unrolled loop over fully visible tiles) or picked
+  // at run time (a few tiles per wave).  kIdle iterations only load for the workgroup.
+  constexpr int kNextClean = 0, kNextMasked = 1, kNextNone = 2, kIdle = 3;
+  auto step = [&](auto next_tag, int t, int cur, const float cf) __attribute__((always_inline)) {
+    constexpr int NEXT = decltype(next_tag)::value;
+    const int nxt = cur ^ 1;
+    wait_vmem();  // K(t+1) and V(t), issued one iteration ago, have landed
     barrier();
-    if (t + 2 < ntiles) load_tile(Kh, t + 2, kl);
-    if (t < ntiles) load_tile(Vh, t, vl);
-    if constexpr (MODE == kDrain) pv(vp);
-    if constexpr (MODE == kClean || MODE == kMasked) {
-      // ---- prepare: the lazy maximum check (fully visible tile) or mask + exact update
-      float cf, m_use[QT], alpha[QT];
-      bool raise;
-      if constexpr (MODE == kClean) {
-        float tm[QT];
+    if (t + 2 < ntiles) load_tile(Kh, t + 2, kbuf[cur]);  // over K(t), read in iteration t-1
+    if (t + 1 < ntiles) load_tile(Vh, t + 1, vbuf[nxt]);  // over V(t-1), read in iteration t-1
+    if constexpr (NEXT == kIdle) return;
+    else {
+      // phase 1: 12 P units over the DS k-steps of S(t+1) (P only when there is no next tile)
+      auto ph1 = [&](int ds) {
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float e = s[0][qt][0];
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) e = NEG ? fminf(e, s[kt][qt][r]) : fmaxf(e, s[kt][qt][r]);
-          e = NEG ? min_halves(e) : max_halves(e);
-          tm[qt] = e * c_log2;
-          alpha[qt] = 1.f;
-        }
-        bool over = false;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) over |= tm[qt] > m_run[qt] + kLazyRescale;
-        raise = __builtin_amdgcn_readfirstlane(__any(over));
-        if (raise) {
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            const float m_new = fmaxf(m_run[qt], tm[qt]);
-            alpha[qt] = fast_exp2(m_run[qt] - m_new);
-            m_run[qt] = m_new;
-          }
-        }
-        cf = c_log2;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) m_use[qt] = m_run[qt];
+        for (int x = 0; x < 12; ++x)
+          if (x * DS / 12 == ds) punit(cur, x / 4, x % 4, cf);
+      };
+      if constexpr (NEXT != kNextNone) {
+        scores(nxt, kbuf[nxt], ph1);
       } else {
-        const int key0 = t * kFwdBc;
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int query = qw + 32 * qt + l32;
-          float mx = -INFINITY;
+        for (int ds = 0; ds < DS; ++ds) ph1(ds);
+      }
+      // phase 2a: 2 DT MFMAs; 4 P units then 4 extreme units
+      pv(vbuf[cur], 0, [&](int i) {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+        for (int x = 0; x < 8; ++x)
+          if (x * 2 * DT / 8 == i) {
+            if (x < 4) punit(cur, 3, x, cf);
+            else if (NEXT == kNextClean) xunit(nxt, x - 4);
+          }
+      });
+      // phase 2b: 2 DT MFMAs; 4 extreme units
+      pv(vbuf[cur], 2, [&](int i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-              const bool vis = (key < L) & (!CAUSAL | (key <= query));
-              const float v = vis ? s[kt][qt][r] * c_log2 : -INFINITY;
-              s[kt][qt][r] = v;
-              mx = fmaxf(mx, v);
-            }
-          mx = max_halves(mx);
-          const float m_new = fmaxf(m_run[qt], mx);
-          m_use[qt] = (m_new == -INFINITY) ? 0.f : m_new;
-          alpha[qt] = fast_exp2(m_run[qt] - m_use[qt]);
-          m_run[qt] = m_new;
+        for (int x = 0; x < 4; ++x)
+          if (x * 2 * DT / 4 == i && NEXT == kNextClean) xunit(nxt, 4 + x);
+      });
+      if constexpr (NEXT == kNextClean) {
+        const float tm = (NEG ? min_halves(ext) : max_halves(ext)) * c_log2;
+        if (__builtin_amdgcn_readfirstlane(__any(tm > m_run + kLazyRescale))) {
+          const float m_new = fmaxf(m_run, tm);
+          const float alpha = fast_exp2(m_p - m_new);
+          m_run = m_new;
+          m_p = m_new;
+          rescale(alpha);
         }
-        cf = 1.f;
-        bool changed = false;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) changed |= alpha[qt] != 1.f;
-        raise = __builtin_amdgcn_readfirstlane(__any(changed));
+      } else if constexpr (NEXT == kNextMasked) {
+        const float alpha = mask_update(nxt, t + 1);
+        if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) rescale(alpha);
       }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) l_run[qt] *= alpha[qt];
-      __builtin_amdgcn_sched_barrier(0);
-
-      // ---- O += P(t-1) V(t-1) on the matrix cores, interleaved with P(t) on the VALU
-      probs(cf, m_use);
-      pv(vp);
-      // 4 DT steps of (2 transposing reads -> 2 MFMAs), each MFMA followed by its share of the VALU work
-      pipe_schedule<4 * DT, 2, QT, VALU3 / (4 * DT * QT), 2, 0>();
-      // Pin P(t) and the row sums here: without a use inside this phase the compiler sinks their
-      // computation past the matrix-core work it is meant to overlap.
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(pn[qt][ks]));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(l_run[qt]));
-      __builtin_amdgcn_sched_barrier(0);
-      if (raise) {  // O carries P(t-1) at the old maximum: scale it to the new one
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha[qt];
-      }
-      // ---- S(t+1) = K(t+1) Q^T
-      scores(kn, s);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) pf[qt][ks] = pn[qt][ks];
     }
   };
-  // even t: K(t+1) in kbuf1, K(t+2) -> kbuf0, V(t-1) in vbuf1, V(t) -> vbuf0; odd t: the other way
-  // round.  Outside the unrolled clean loop the buffers are picked at run time (one copy of each
-  // form; two copies of the masked form would not fit the register budget).
-  auto at = [&](auto mode, int t) __attribute__((always_inline)) {
-    const bool odd = t & 1;
-    step(mode, t, odd ? kbuf0 : kbuf1, odd ? kbuf1 : kbuf0, odd ? vbuf0 : vbuf1, odd ? vbuf1 : vbuf0);
-  };
-  using Clean = std::integral_constant<int, kClean>;
-  const int n_clean = min(n_full, n_wave);
+
+  using NC = std::integral_constant<int, kNextClean>;
+  // fully visible tile followed by a fully visible tile: compile-time sets and buffers
   int t = 0;
-  for (; t + 1 < n_clean; t += 2) {
-    step(Clean{}, t, kbuf1, kbuf0, vbuf1, vbuf0);
-    step(Clean{}, t + 1, kbuf0, kbuf1, vbuf0, vbuf1);
+  const int n_cc = n_clean - 1;  // iterations t with tiles t and t+1 both fully visible
+  for (; t + 1 < n_cc; t += 2) {
+    step(NC{}, t, 0, c_log2);
+    step(NC{}, t + 1, 1, c_log2);
   }
-  if (t < n_clean) step(Clean{}, t++, kbuf1, kbuf0, vbuf1, vbuf0);
-  for (; t < n_wave; ++t) at(std::integral_constant<int, kMasked>{}, t);
-  at(std::integral_constant<int, kDrain>{}, t++);  // t == n_wave <= ntiles
-  for (; t <= ntiles; ++t) at(std::integral_constant<int, kIdle>{}, t);
+  if (t < n_cc) {
+    step(NC{}, t, 0, c_log2);
+    ++t;
+  }
+  // the rest: S(t) is moved to set 0 first, and every remaining form keeps it there (S(t+1) is
+  // computed into set 1 and moved to set 0 at the end)
+  if (t & 1) {
+    s[0][0] = s[1][0];
+    s[0][1] = s[1][1];
+  }
+  auto run = [&](auto next_tag, int t) __attribute__((always_inline)) {
+    const bool odd = t & 1;
+    FA_LDS char* kb_cur = odd ? kbuf[1] : kbuf[0];
+    FA_LDS char* kb_nxt = odd ? kbuf[0] : kbuf[1];
+    FA_LDS char* vb_cur = odd ? vbuf[1] : vbuf[0];
+    FA_LDS char* vb_nxt = odd ? vbuf[0] : vbuf[1];
+    constexpr int NEXT = decltype(next_tag)::value;
+    const float cf = t < n_clean ? c_log2 : 1.f;
+    wait_vmem();
+    barrier();
+    if (t + 2 < ntiles) load_tile(Kh, t + 2, kb_cur);
+    if (t + 1 < ntiles) load_tile(Vh, t + 1, vb_nxt);
+    if constexpr (NEXT != kIdle) {
+      auto ph1 = [&](int ds) {
+#pragma unroll
+        for (int x = 0; x < 12; ++x)
+          if (x * DS / 12 == ds) punit(0, x / 4, x % 4, cf);
+      };
+      if constexpr (NEXT == kNextMasked) {
+        scores(1, kb_nxt, ph1);
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) ph1(ds);
+      }
+      pv(vb_cur, 0, [&](int i) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (x * 2 * DT / 4 == i) punit(0, 3, x, cf);
+      });
+      pv(vb_cur, 2, [](int) {});
+      if constexpr (NEXT == kNextMasked) {
+        const float alpha = mask_update(1, t + 1);
+        if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) rescale(alpha);
+        s[0][0] = s[1][0];
+        s[0][1] = s[1][1];
+      }
+    }
+  };
+  for (; t + 1 < n_wave; ++t) run(std::integral_constant<int, kNextMasked>{}, t);
+  if (t < n_wave) run(std::integral_constant<int, kNextNone>{}, t++);
+  for (; t < ntiles; ++t) run(std::integral_constant<int, kIdle>{}, t);
 
   // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int query = qw + 32 * qt + l32;
-    const float l = add_halves(l_run[qt]);
+  {
+    const float l = add_halves(l_run);
     const bool has = l > 0.f;
     const float inv = has ? 1.f / l : 0.f;
     if (query < N) {
-      if (half == 0) LSE[row0 + query] = has ? (m_run[qt] + __log2f(l)) * kLn2 : -INFINITY;
+      if (half == 0) LSE[row0 + query] = has ? (m_p + __log2f(l)) * kLn2 : -INFINITY;
       __bf16* orow = O + (row0 + query) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int d0 = 32 * dt + 8 * gq + 4 * half;
-          const bf16x4 v4 = pack4(acc[qt][dt][4 * gq] * inv, acc[qt][dt][4 * gq + 1] * inv,
-                                  acc[qt][dt][4 * gq + 2] * inv, acc[qt][dt][4 * gq + 3] * inv);
+          const bf16x4 v4 = pack4(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv, acc[dt][4 * gq + 2] * inv,
+                                  acc[dt][4 * gq + 3] * inv);
           *(bf16x4*)(orow + d0) = v4;
         }
     }

@@ -6,10 +6,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#ifndef FA_FWD_ROWS_PER_WAVE
-#define FA_FWD_ROWS_PER_WAVE 32  // query rows per wave of the bf16 forward kernel (32 or 64)
-#endif
-
 namespace fa {
 
 struct Problem {
