@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     qf[ds] = *(const bf16x8*)(Qh + (int64_t)qrow * D + 16 * ds + 8 * half);
     gf[ds] = *(const bf16x8*)(dOh + (int64_t)qrow * D + 16 * ds + 8 * half);
   }
-  const float lse2 = LSE2[row0 + qrow];  // LSE log2(e) of this lane's query
-  const float del = DELTA[row0 + qrow];  // D = sum_c dO_c O_c
+  float lse2 = LSE2[row0 + qrow];        // LSE log2(e) of this lane's query
+  float del = DELTA[row0 + qrow];        // D = sum_c dO_c O_c
 
   f32x16 acc[DT];  // dQ^T [d][q]: lane = query column, rows d = 32 dt + 8 (r/4) + 4 half + r%4
 #pragma unroll
@@ -229,6 +229,16 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
       load_tile(Kh, i, kst[i]);
       load_tile(Vh, i, vst[i]);
     }
+  // The stationary operands are complete here; saying so (an unconditional use) keeps the compiler
+  // from waiting for them -- and, as it cannot tell them apart, for the tile loads in flight --
+  // inside the loop.
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    pin(qf[ds]);
+    pin(gf[ds]);
+  }
+  pin(lse2);
+  pin(del);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2 % NS>;

@@ -180,6 +180,10 @@ __device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0
 // its side of the barrier; the LDS reads issued before it have all been consumed (and so have
 // completed) by then, so no lgkmcnt wait is needed for the stage that is reloaded after it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Keeps the computation of x where it stands: the (empty) volatile statement consumes and
+// redefines x, so the code that produces x is not moved past later volatile statements (barriers).
+template <class T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 // Value of x in lane l ^ 32 combined with x by max / add (one v_permlane32_swap).
 __device__ __forceinline__ float max_halves(float x) {

@@ -271,6 +271,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   }
   wait_vmem();
   barrier();
+  // The Q fragments are complete here; saying so (an unconditional use) keeps the compiler from
+  // waiting for them -- and, as it cannot tell them apart, for the tile loads in flight -- inside
+  // the loop.
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) pin(qf[ds]);
   if (n_wave > 0) {
     scores(0, kbuf[0], [](int) {});
     if (n_clean > 0) exact_update(0);
