@@ -4,4 +4,4 @@ Importable only by tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
 leg.  The product path never imports it.
 """
 from .attention import (backward, backward_keys, backward_rows, forward, forward_rows,  # noqa: F401
-                        key_lengths, row_stats, visible)
+                        key_lengths, row_stats, visible, block_count, MASK_BLOCK)

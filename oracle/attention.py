@@ -32,8 +32,14 @@ Readings where the pages are silent (each is also listed in the design doc):
   (top-left aligned, Nq = Nk = N).  Key padding keeps key j of batch b iff
   j < L_b with L_b = clamp(seqlens[b], 0, N); both masks combine by AND;
   padded *query* rows are computed normally;
-* a row with no visible key (only possible when L_b = 0) has O = 0,
-  LSE = -inf and contributes no gradient;
+* block-sparse attention (the tiling applied to a sparse pattern: promptingindex
+  page, "Benchmark results: speed records without any approximation"; NOTE-005,
+  "Key components" and "Limitations", where it is approximate relative to dense
+  attention): an optional [B, H, ceil(N/128), ceil(N/128)] block mask; key j is
+  visible to query i only if block (i // 128, j // 128) is nonzero.  It combines
+  with the other masks by AND, and the result is exact for the masked problem;
+* a row with no visible key (L_b = 0, or every block of its row masked out)
+  has O = 0, LSE = -inf and contributes no gradient;
 * backward of the loss sum(dO * O): dV = Pᵀ dO, dP = dO Vᵀ,
   D_i = sum_j P_ij dP_ij, dS = P * (dP - D), dQ = scale * dS K,
   dK = scale * dSᵀ Q -- the chain rule through the definition above (the pages
@@ -49,6 +55,7 @@ import math
 import torch
 
 F64 = torch.float64
+MASK_BLOCK = 128  # rows and columns of one block of the block-sparse mask
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -65,19 +72,42 @@ def key_lengths(B: int, N: int, seqlens) -> list[int]:
     return [min(max(int(x), 0), N) for x in s]
 
 
-def visible(N: int, causal: bool, L: int, rows=None) -> torch.Tensor:
+def block_count(N: int) -> int:
+    """Blocks per side of the block-sparse mask: ceil(N / 128)."""
+    return (N + MASK_BLOCK - 1) // MASK_BLOCK
+
+
+def visible(N: int, causal: bool, L: int, rows=None, blocks=None) -> torch.Tensor:
     """Boolean visibility vis[i, j] for query rows ``rows`` (default all) and keys 0..N-1.
 
     Masking step of the attention chain ("Why attention is memory-bound" section
     of the promptingindex page), read as: key j is visible to query i iff
-    j < L (key padding) and, when causal, j <= i.
+    j < L (key padding) and, when causal, j <= i, and, when ``blocks`` (this
+    head's [ceil(N/128), ceil(N/128)] block mask) is given, block
+    (i // 128, j // 128) is nonzero.
     """
     i = torch.arange(N, dtype=torch.int64) if rows is None else torch.as_tensor(rows, dtype=torch.int64)
     j = torch.arange(N, dtype=torch.int64)
     vis = (j[None, :] < L).expand(i.numel(), N).clone()
     if causal:
         vis &= j[None, :] <= i[:, None]
+    if blocks is not None:
+        bm = torch.as_tensor(blocks).to("cpu") != 0
+        nb = block_count(N)
+        if tuple(bm.shape) != (nb, nb):
+            raise ValueError(f"block mask of one head must be [{nb}, {nb}]")
+        vis &= bm[(i // MASK_BLOCK)[:, None], (j // MASK_BLOCK)[None, :]]
     return vis
+
+
+def _head_blocks(block_mask, B: int, H: int, b: int, h: int):
+    """The [nb, nb] block mask of head (b, h), or None for dense attention."""
+    if block_mask is None:
+        return None
+    bm = torch.as_tensor(block_mask).to("cpu")
+    if bm.dim() != 4 or bm.shape[0] != B or bm.shape[1] != H:
+        raise ValueError("block mask must be [B, H, ceil(N/128), ceil(N/128)]")
+    return bm[b, h]
 
 
 def _scores(q, k, scale, vis):
@@ -104,7 +134,7 @@ def _probs(s, lse):
     return torch.where(empty[:, None], torch.zeros_like(p), p)
 
 
-def forward(q, k, v, scale: float, causal: bool = False, seqlens=None):
+def forward(q, k, v, scale: float, causal: bool = False, seqlens=None, block_mask=None):
     """O and LSE for [B, H, N, d] inputs; returns fp64 tensors O [B,H,N,d] and LSE [B,H,N].
 
     NOTE-005 "Key results" Theorem 1 (O = softmax(QKᵀ)V) with the scaling and
@@ -118,8 +148,10 @@ def forward(q, k, v, scale: float, causal: bool = False, seqlens=None):
     o = torch.empty(B, H, N, v.shape[-1], dtype=F64)
     lse = torch.empty(B, H, N, dtype=F64)
     for b in range(B):
-        vis = visible(N, causal, L[b])
+        vis_b = visible(N, causal, L[b])
         for h in range(H):
+            blocks = _head_blocks(block_mask, B, H, b, h)
+            vis = vis_b if blocks is None else visible(N, causal, L[b], blocks=blocks)
             s = _scores(q[b, h], k[b, h], scale, vis)
             lse[b, h] = _row_lse(s)
             p = _probs(s, lse[b, h])
@@ -127,7 +159,7 @@ def forward(q, k, v, scale: float, causal: bool = False, seqlens=None):
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None):
+def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None, block_mask=None):
     """dQ, dK, dV (fp64) of the loss sum(dO * O) through the definition of ``forward``.
 
     The pages state only that the backward recomputes the attention block from
@@ -144,8 +176,10 @@ def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None):
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     for b in range(B):
-        vis = visible(N, causal, L[b])
+        vis_b = visible(N, causal, L[b])
         for h in range(H):
+            blocks = _head_blocks(block_mask, B, H, b, h)
+            vis = vis_b if blocks is None else visible(N, causal, L[b], blocks=blocks)
             s = _scores(q[b, h], k[b, h], scale, vis)
             p = _probs(s, _row_lse(s))
             dv[b, h] = torch.matmul(p.transpose(0, 1), do[b, h])
@@ -163,24 +197,26 @@ def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None):
 # choose which rows (or which key columns) are produced.
 # ----------------------------------------------------------------------------
 
-def forward_rows(q, k, v, scale: float, causal: bool, seqlens, b: int, h: int, rows):
+def forward_rows(q, k, v, scale: float, causal: bool, seqlens, b: int, h: int, rows, block_mask=None):
     """O[rows] and LSE[rows] of head (b, h), each row over all N keys (same definition as ``forward``)."""
     qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
     N = kh.shape[0]
     rows = torch.as_tensor(rows, dtype=torch.int64)
     L = key_lengths(q.shape[0], N, seqlens)[b]
-    s = _scores(qh[rows], kh, float(scale), visible(N, causal, L, rows))
+    blocks = _head_blocks(block_mask, q.shape[0], q.shape[1], b, h)
+    s = _scores(qh[rows], kh, float(scale), visible(N, causal, L, rows, blocks))
     lse = _row_lse(s)
     return torch.matmul(_probs(s, lse), vh), lse
 
 
-def backward_rows(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, rows):
+def backward_rows(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, rows, block_mask=None):
     """dQ[rows] of head (b, h).  Row i of dQ needs only row i of P, dP and D."""
     qh, kh, vh, doh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h])
     N = kh.shape[0]
     rows = torch.as_tensor(rows, dtype=torch.int64)
     L = key_lengths(q.shape[0], N, seqlens)[b]
-    s = _scores(qh[rows], kh, float(scale), visible(N, causal, L, rows))
+    blocks = _head_blocks(block_mask, q.shape[0], q.shape[1], b, h)
+    s = _scores(qh[rows], kh, float(scale), visible(N, causal, L, rows, blocks))
     p = _probs(s, _row_lse(s))
     dp = torch.matmul(doh[rows], vh.transpose(0, 1))
     D = torch.sum(p * dp, dim=1, keepdim=True)
@@ -188,7 +224,7 @@ def backward_rows(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: i
 
 
 def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, chunk: int = 1024,
-              progress=None):
+              progress=None, block_mask=None):
     """LSE_i and D_i for every row of head (b, h), computed ``chunk`` complete rows at a time.
 
     D_i = sum_j P_ij dP_ij is evaluated as dO_i . O_i, which equals it because
@@ -202,7 +238,7 @@ def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, 
     doh = _f64(do[b, h])
     for r0 in range(0, N, chunk):
         rows = torch.arange(r0, min(N, r0 + chunk))
-        o_r, lse_r = forward_rows(q, k, v, scale, causal, seqlens, b, h, rows)
+        o_r, lse_r = forward_rows(q, k, v, scale, causal, seqlens, b, h, rows, block_mask)
         lse[rows] = lse_r
         D[rows] = torch.sum(o_r * doh[rows], dim=1)
         if progress is not None:
@@ -210,7 +246,8 @@ def row_stats(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, 
     return lse, D
 
 
-def backward_keys(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, keys, lse, D):
+def backward_keys(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: int, keys, lse, D,
+                  block_mask=None):
     """dK[keys], dV[keys] of head (b, h) from the full-row statistics LSE and D of ``row_stats``.
 
     Column j of P needs LSE_i of every row i; column j of dS needs D_i of every
@@ -220,7 +257,8 @@ def backward_keys(q, k, v, do, scale: float, causal: bool, seqlens, b: int, h: i
     N = qh.shape[0]
     keys = torch.as_tensor(keys, dtype=torch.int64)
     L = key_lengths(q.shape[0], N, seqlens)[b]
-    vis_t = visible(N, causal, L)[:, keys]                       # [N, |keys|]
+    blocks = _head_blocks(block_mask, q.shape[0], q.shape[1], b, h)
+    vis_t = visible(N, causal, L, blocks=blocks)[:, keys]        # [N, |keys|]
     st = (torch.matmul(qh, kh[keys].transpose(0, 1)) * float(scale)).masked_fill(~vis_t, -math.inf)
     lse = _f64(lse)
     empty = torch.isinf(lse) & (lse < 0)

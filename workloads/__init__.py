@@ -108,3 +108,26 @@ def draw_custom(B, H, N, d, dtype="bf16", causal=False, seqlens=None, q_std=1.0,
         out["seqlens"] = torch.as_tensor(seqlens, dtype=torch.int32)
     return out
 
+
+def draw_block_mask(B, H, N, pattern="random", density=0.5, window=1, seed=0):
+    """A [B, H, ceil(N/128), ceil(N/128)] uint8 block mask (1 = block visible) for block-sparse tests.
+
+    pattern "random": each block visible with probability ``density`` (a seeded Bernoulli draw;
+    some rows may end up with no visible block).  "local": query block i sees key blocks
+    i-window .. i+window.  "local+global": "local" plus the first key block for every query block
+    (and every key block for the first query block).  Only random numbers and index patterns.
+    """
+    nb = (N + 127) // 128
+    if pattern == "random":
+        g = torch.Generator("cpu").manual_seed(seed)
+        m = (torch.rand((B, H, nb, nb), generator=g) < density).to(torch.uint8)
+    else:
+        i = torch.arange(nb)
+        m = ((i[:, None] - i[None, :]).abs() <= window)
+        if pattern == "local+global":
+            m = m | (i[None, :] == 0) | (i[:, None] == 0)
+        elif pattern != "local":
+            raise ValueError(pattern)
+        m = m.to(torch.uint8)[None, None].expand(B, H, nb, nb).contiguous()
+    return m
+
