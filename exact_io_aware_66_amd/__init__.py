@@ -7,6 +7,8 @@ missing or a call is unsupported, these functions raise.
     fa_forward(q, k, v, o, lse, scale, causal, seqlens)            # C-ABI names, caller-owned outputs
     fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace)
     fa_backward_workspace_size(B, H, N, d, dtype)
+    fa_forward_block_sparse(q, k, v, o, lse, scale, causal, seqlens, block_mask)
+    fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace)
     forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
     backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
 """
@@ -26,7 +28,9 @@ FA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_MISALIGNED",
           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
-           "fa_backward_dq", "fa_status_string", "fa_last_error")
+           "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_status_string",
+           "fa_last_error")
+MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
 
 _lib = None
 
@@ -56,6 +60,10 @@ def load(path: str = LIB_PATH):
     lib.fa_backward_dkdv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
     lib.fa_backward_dq.restype = i
+    lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, vp]
+    lib.fa_forward_block_sparse.restype = i
+    lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
+    lib.fa_backward_block_sparse.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -114,6 +122,16 @@ def _seqlens(seqlens, B, device):
     return seqlens
 
 
+def _block_mask(block_mask, B, H, N, device):
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    if not (block_mask.is_cuda and block_mask.dtype == torch.uint8 and block_mask.is_contiguous()
+            and tuple(block_mask.shape) == (B, H, nb, nb)):
+        raise ValueError(f"block_mask must be a contiguous uint8 device tensor of shape [B, H, {nb}, {nb}]")
+    if block_mask.device != device:
+        raise ValueError("block_mask must be on the tensors' device")
+    return block_mask
+
+
 def fa_backward_workspace_size(B: int, H: int, N: int, d: int, dtype) -> int:
     code = FA_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load().fa_backward_workspace_size(B, H, N, d, code))
@@ -140,6 +158,32 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fa
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                            _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_forward_block_sparse(q, k, v, o, lse, scale: float, causal: bool, seqlens, block_mask, stream=None) -> None:
+    """C-ABI fa_forward_block_sparse: block_mask is uint8 [B, H, ceil(N/128), ceil(N/128)] on the device."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, lse)
+    seqlens = _seqlens(seqlens, B, q.device)
+    block_mask = _block_mask(block_mask, B, H, N, q.device)
+    _check(lib.fa_forward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                       int(bool(causal)), _ptr(seqlens), _ptr(block_mask), _dtype_code(q),
+                                       _stream(stream)))
+
+
+def fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, seqlens, block_mask,
+                             workspace, stream=None) -> None:
+    """C-ABI fa_backward_block_sparse (same block mask as the forward)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    block_mask = _block_mask(block_mask, B, H, N, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens),
+                                        _ptr(block_mask), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
@@ -181,23 +225,31 @@ def _default_scale(d: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
 
 
-def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=None, stream=None):
-    """Allocate O and LSE and run fa_forward; returns (o, lse)."""
+def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=None, stream=None, block_mask=None):
+    """Allocate O and LSE and run fa_forward (fa_forward_block_sparse with a block mask); returns (o, lse)."""
     B, H, N, d = _dims(q)
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_forward(q, k, v, o, lse, scale, causal, seqlens, stream)
+    if block_mask is None:
+        fa_forward(q, k, v, o, lse, scale, causal, seqlens, stream)
+    else:
+        fa_forward_block_sparse(q, k, v, o, lse, scale, causal, seqlens, block_mask, stream)
     return o, lse
 
 
 def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, seqlens=None, stream=None,
-             workspace=None):
-    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_backward; returns (dq, dk, dv)."""
+             workspace=None, block_mask=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_backward (fa_backward_block_sparse
+    with a block mask); returns (dq, dk, dv)."""
     B, H, N, d = _dims(q)
     scale = _default_scale(d) if scale is None else scale
     if workspace is None:
         workspace = torch.empty(fa_backward_workspace_size(B, H, N, d, q.dtype), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace, stream)
+    if block_mask is None:
+        fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace, stream)
+    else:
+        fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace,
+                                 stream)
     return dq, dk, dv

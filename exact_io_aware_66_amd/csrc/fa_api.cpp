@@ -181,9 +181,20 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d, fa_dtype_t dtype) 
   return fa::bwd_workspace_layout(B, H, N, d, dtype == FA_DTYPE_BF16).total;
 }
 
-fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                       float scale, int causal, const int32_t* seqlens, fa_dtype_t dtype, void* stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+fa_status_t check_block_mask(const uint8_t* block_mask, int N) {
+  if (block_mask == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "block_mask is NULL");
+  if (N > FA_MASK_MAX_N)
+    return fail(FA_ERR_UNSUPPORTED, "block-sparse attention supports N <= %d (got %d)", FA_MASK_MAX_N, N);
+  return FA_OK;
+}
+
+fa_status_t forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                         float scale, int causal, const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype,
+                         void* stream) {
   fa_status_t s;
   if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
   if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
@@ -194,29 +205,68 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
     return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
   if ((s = check_head_bytes(N, d, dtype)) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
-  const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  p.block_mask = block_mask;
   const hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, q, k, v, o, lse)
                                : fa::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse);
   if (e != hipSuccess) return hip_fail(e, "fa_forward launch");
   return FA_OK;
 }
 
-
-fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                        void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                        const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  g_last_error[0] = '\0';
+fa_status_t backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                          void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                          const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   fa_status_t s;
   if ((s = validate_stage(q, k, v, dO, lse, {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}}, B, H, N, d, scale, seqlens, dtype,
                           workspace, workspace_bytes)) != FA_OK)
     return s;
   if ((s = check_tensor(o, "o")) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
-  const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  p.block_mask = block_mask;
   if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
   if ((s = run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace)) != FA_OK) return s;
   return run_dq(p, dtype, q, k, v, dO, lse, dq, workspace);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                       float scale, int causal, const int32_t* seqlens, fa_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, nullptr, dtype, stream);
+}
+
+fa_status_t fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                    int N, int d, float scale, int causal, const int32_t* seqlens,
+                                    const uint8_t* block_mask, fa_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_block_mask(block_mask, N)) != FA_OK) return s;
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, block_mask, dtype, stream);
+}
+
+fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                        void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                        const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_last_error[0] = '\0';
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, nullptr, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+fa_status_t fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                     float scale, int causal, const int32_t* seqlens, const uint8_t* block_mask,
+                                     fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_block_mask(block_mask, N)) != FA_OK) return s;
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, block_mask, dtype,
+                       workspace, workspace_bytes, stream);
 }
 
 fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,

@@ -77,13 +77,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 template <int D>
 constexpr int bwd_rows_per_tile() { return D == 128 ? 32 : 64; }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                           const float* __restrict__ LSE2,
                                                           const float* __restrict__ DELTA, __bf16* __restrict__ dK,
                                                           __bf16* __restrict__ dV, int H, int N, float scale,
-                                                          float c_log2, const int32_t* __restrict__ seqlens, int BH) {
+                                                          float c_log2, const int32_t* __restrict__ seqlens,
+                                                          const uint8_t* __restrict__ bmask, int BH) {
   constexpr int BR = bwd_rows_per_tile<D>();  // query rows per tile
   constexpr int QS = BR / 32;                 // 32-row halves of a tile
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -102,6 +103,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   __shared__ __attribute__((aligned(1024))) char st1_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st3_raw[STAGE];
+  // block-sparse: the visible query tiles of this key block, in order (kBwdBc / BR per mask block)
+  __shared__ uint16_t tlist_raw[SPARSE ? (kBwdBc / BR) * kMaxMaskBlocks : 1];
+  __shared__ int tcount_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -157,7 +161,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 
     const int nqt = (N + BR - 1) / BR;
     const int it0 = CAUSAL ? (k0 / BR) : 0;
-    const int count = nqt - it0;  // query tiles this key block visits (>= 1)
+    int count = nqt - it0;  // query tiles this key block visits (>= 1)
+    // Block-sparse: the steps walk the list of visible query tiles (in tile order); the masked head
+    // (the causal diagonal block) is present only when that block is visible, and then it is the
+    // list's head, tiles it0 .. it0+HEAD-1 as in the dense walk.
+    const FA_LDS uint16_t* const tlist = (const FA_LDS uint16_t*)tlist_raw;
+    bool head_visible = true;
+    if constexpr (SPARSE) {
+      const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+      const uint8_t* bcol = bmask + (int64_t)bh * nb * nb + kblock;
+      if (wave == 0)
+        compact_tiles<kBwdBc / BR>((FA_LDS uint16_t*)tlist_raw, (FA_LDS int*)&tcount_raw, it0 * BR / kMaskBlock, nb,
+                                   nqt, [&](int qb) { return bcol[(int64_t)qb * nb] != 0 ? 1 : 0; });
+      __syncthreads();
+      count = *(volatile FA_LDS int*)&tcount_raw;
+      head_visible = CAUSAL && count > 0 && list_tile(tlist[0]) == it0;
+    }
 
     // Tile loads: buffer loads straight into LDS.  Rows past N read as zeros (the buffer ends at the
     // head's last row), and a zero Q and dO row adds exactly nothing to dK and dV, so the ragged last
@@ -173,7 +192,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     // Wave w fetches 64 rows of statistic w & 1 (0: LSE log2 e, 1: D) into its own 256-byte slot.
     const float* stat = (wave & 1) ? DELTA + row0 : LSE2 + row0;
     auto load_tile = [&](int u, FA_LDS char* dst) {
-      const int qbase = (it0 + u) * BR;
+      const int qbase = (SPARSE ? list_tile(tlist[u]) : it0 + u) * BR;
       const int left = N - qbase;  // rows of the head from qbase on (>= 1)
       const u32x4 rq = make_rsrc(Qh + (int64_t)qbase * D, left * D * 2);
       const u32x4 rg = make_rsrc(dOh + (int64_t)qbase * D, left * D * 2);
@@ -332,30 +351,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
 
-    load_tile(0, st[0]);
-    if (count > 1) load_tile(1, st[1]);
-    if (count > 2) load_tile(2, st[2]);
-    wait_vmem();
-    barrier();
-    scores(I0{}, st[0], [](int) {});
+    // fully visible tiles from u on, four per iteration so that stages and score sets stay
+    // compile-time (the walk starts in phase PH0 = u % 4)
+    auto visible_tiles = [&](auto ph0, int u) __attribute__((always_inline)) {
+      constexpr int PH0 = decltype(ph0)::value;
+      for (; u + 3 < count; u += 4) {
+        at(C{}, std::integral_constant<int, PH0>{}, u);
+        at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
+        at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
+        at(C{}, std::integral_constant<int, (PH0 + 3) % 4>{}, u + 3);
+      }
+      if (u < count) at(C{}, std::integral_constant<int, PH0>{}, u);
+      if (u + 1 < count) at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
+      if (u + 2 < count) at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
+    };
 
-    // masked head (causal): tiles 0 .. HEAD-1
-    if constexpr (HEAD >= 1) at(M{}, I0{}, 0);
-    if constexpr (HEAD >= 2) { if (count > 1) at(M{}, I1{}, 1); }
-    if constexpr (HEAD >= 3) { if (count > 2) at(M{}, I2{}, 2); }
-    if constexpr (HEAD >= 4) { if (count > 3) at(M{}, I3{}, 3); }
-    // fully visible tiles, four per iteration so that stages and score sets stay compile-time
-    constexpr int PH0 = HEAD % 4;
-    int u = HEAD;
-    for (; u + 3 < count; u += 4) {
-      at(C{}, std::integral_constant<int, PH0>{}, u);
-      at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
-      at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
-      at(C{}, std::integral_constant<int, (PH0 + 3) % 4>{}, u + 3);
+    if (!SPARSE || count > 0) {
+      load_tile(0, st[0]);
+      if (count > 1) load_tile(1, st[1]);
+      if (count > 2) load_tile(2, st[2]);
+      wait_vmem();
+      barrier();
+      scores(I0{}, st[0], [](int) {});
+
+      if (!SPARSE || head_visible || !CAUSAL) {
+        // masked head (causal): tiles 0 .. HEAD-1
+        if constexpr (HEAD >= 1) at(M{}, I0{}, 0);
+        if constexpr (HEAD >= 2) { if (count > 1) at(M{}, I1{}, 1); }
+        if constexpr (HEAD >= 3) { if (count > 2) at(M{}, I2{}, 2); }
+        if constexpr (HEAD >= 4) { if (count > 3) at(M{}, I3{}, 3); }
+        visible_tiles(std::integral_constant<int, HEAD % 4>{}, HEAD);
+      } else {
+        visible_tiles(I0{}, 0);  // (block-sparse, causal) the diagonal block is masked out: no head
+      }
     }
-    if (u < count) at(C{}, std::integral_constant<int, PH0>{}, u);
-    if (u + 1 < count) at(C{}, std::integral_constant<int, (PH0 + 1) % 4>{}, u + 1);
-    if (u + 2 < count) at(C{}, std::integral_constant<int, (PH0 + 2) % 4>{}, u + 2);
   }
 
   // ---- dK = scale dS^T Q, dV: lane holds key my_key, d = 32 dt + 8 gq + 4 half + 0..3.  Keys at
@@ -382,26 +411,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
 hipError_t launch_dkdv(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                        const float* delta, void* dk, void* dv) {
   const int nkb = (p.N + kBwdBc - 1) / kBwdBc;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED>), dim3((unsigned)(nkb * BH)), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE>), dim3((unsigned)(nkb * BH)), dim3(256), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta, (__bf16*)dk,
-                     (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, BH);
+                     (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask, BH);
   return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t launch_dkdv_m(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse2, const float* delta, void* dk, void* dv) {
+  const bool pad = p.seqlens != nullptr;
+  if (p.causal)
+    return pad ? launch_dkdv<D, true, true, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv)
+               : launch_dkdv<D, true, false, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv);
+  return pad ? launch_dkdv<D, false, true, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv)
+             : launch_dkdv<D, false, false, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv);
 }
 
 template <int D>
 hipError_t launch_dkdv_d(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                          const float* lse2, const float* delta, void* dk, void* dv) {
-  const bool pad = p.seqlens != nullptr;
-  if (p.causal)
-    return pad ? launch_dkdv<D, true, true>(p, q, k, v, dO, lse2, delta, dk, dv)
-               : launch_dkdv<D, true, false>(p, q, k, v, dO, lse2, delta, dk, dv);
-  return pad ? launch_dkdv<D, false, true>(p, q, k, v, dO, lse2, delta, dk, dv)
-             : launch_dkdv<D, false, false>(p, q, k, v, dO, lse2, delta, dk, dv);
+  return p.block_mask != nullptr ? launch_dkdv_m<D, true>(p, q, k, v, dO, lse2, delta, dk, dv)
+                                 : launch_dkdv_m<D, false>(p, q, k, v, dO, lse2, delta, dk, dv);
 }
 
 template <int D, typename T>

@@ -41,13 +41,14 @@ constexpr int kDqRowsPerWave = 32;
 constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // query rows per workgroup
 constexpr int kDqBc = 64;                         // keys per tile
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
 __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         const float* __restrict__ LSE2,
                                                         const float* __restrict__ DELTA, __bf16* __restrict__ dQ,
                                                         int H, int N, float scale, float c_log2,
-                                                        const int32_t* __restrict__ seqlens, int nqb, int BH) {
+                                                        const int32_t* __restrict__ seqlens,
+                                                        const uint8_t* __restrict__ bmask, int nqb, int BH) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kDqBc * D * 2;      // bytes of one K or V tile
   constexpr int LOADS = kDqBc * CH / (64 * kDqWaves);  // 16-byte loads per thread per tile
@@ -62,6 +63,10 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   __shared__ __attribute__((aligned(1024))) char vbuf2_raw[kDqStages > 2 ? TILE : 16];
   FA_LDS char* const kst[3] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw, (FA_LDS char*)kbuf2_raw};
   FA_LDS char* const vst[3] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw, (FA_LDS char*)vbuf2_raw};
+  // block-sparse: the key tiles visible to any of the workgroup's query blocks, in order, with one
+  // flag bit per query block (two tiles per mask block)
+  __shared__ uint16_t tlist_raw[SPARSE ? 2 * kMaxMaskBlocks : 1];
+  __shared__ int tcount_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -92,11 +97,37 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   const int q0 = qblock * kDqBr;
   const int qw = q0 + wave * kDqRowsPerWave;
   const int kv_end = CAUSAL ? min(L, q0 + kDqBr) : L;
-  const int ntiles = (kv_end + kDqBc - 1) / kDqBc;  // tiles the workgroup loads
+  int ntiles = (kv_end + kDqBc - 1) / kDqBc;  // tiles the workgroup loads
   const int wave_end = CAUSAL ? min(L, qw + kDqRowsPerWave) : L;
-  const int n_wave = (wave_end + kDqBc - 1) / kDqBc;  // tiles this wave computes
-  int n_full = L / kDqBc;                             // leading tiles with no hidden pair
+  int n_wave = (wave_end + kDqBc - 1) / kDqBc;  // tiles this wave computes
+  int n_full = L / kDqBc;                       // leading tiles with no hidden pair
   if (CAUSAL) n_full = min(n_full, qw / kDqBc);
+  // Block-sparse: the steps walk the list of tiles visible to some query block of the workgroup;
+  // a wave computes a tile only when its own block's flag is set.  n_wave becomes a list position;
+  // n_full stays a tile index (the masking of a tile depends on where it is, not on the list).
+  const FA_LDS uint16_t* const tlist = (const FA_LDS uint16_t*)tlist_raw;
+  constexpr int kBlocksPerWg = kDqBr / kMaskBlock;
+  const int wbit = (wave * kDqRowsPerWave) / kMaskBlock;  // this wave's query block within the workgroup
+  if constexpr (SPARSE) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const int qb0 = q0 / kMaskBlock;
+    const uint8_t* brow = bmask + ((int64_t)bh * nb + qb0) * nb;
+    if (wave == 0)
+      compact_tiles<kMaskBlock / kDqBc>((FA_LDS uint16_t*)tlist_raw, (FA_LDS int*)&tcount_raw, 0, (ntiles + 1) / 2,
+                                        ntiles, [&](int kb) {
+                                          int f = 0;
+#pragma unroll
+                                          for (int g = 0; g < kBlocksPerWg; ++g)
+                                            if (qb0 + g < nb && brow[(int64_t)g * nb + kb] != 0) f |= 1 << g;
+                                          return f;
+                                        });
+    __syncthreads();
+    const int n = *(volatile FA_LDS int*)&tcount_raw;
+    n_wave = count_below(tlist, n, n_wave);
+    ntiles = n;
+  }
+  auto tix = [&](int t) { return SPARSE ? list_tile(tlist[t]) : t; };
+  auto mine = [&](int t) { return !SPARSE || ((list_flags(tlist[t]) >> wbit) & 1); };
 
   // Q^T and dO^T fragments (B operands): lane holds query qw + l32, d = 16 ds + 8 half .. +7
   const int query = qw + l32;
@@ -126,6 +157,7 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     voff[n] = (uint32_t)(r * D + 8 * c) * 2;
   }
   auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+    t = tix(t);
     const u32x4 rs = make_rsrc(src + (int64_t)t * kDqBc * D, (N - t * kDqBc) * D * 2);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kDqWaves + wave) * 1024);
@@ -221,7 +253,7 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
       load_tile(Kh, t + NS - 1, kst[(S + NS - 1) % NS]);
       load_tile(Vh, t + NS - 1, vst[(S + NS - 1) % NS]);
     }
-    if (t < n_wave) tile(t, kst[S], vst[S]);
+    if (t < n_wave && mine(t)) tile(tix(t), kst[S], vst[S]);
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
@@ -265,24 +297,33 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                   const float* delta, void* dq) {
   const int nqb = (p.N + kDqBr - 1) / kDqBr;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)(nqb * BH)), dim3(kDqWaves * 64), 0, p.stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta, (__bf16*)dq,
-                     p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, nqb, BH);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE>), dim3((unsigned)(nqb * BH)), dim3(kDqWaves * 64), 0,
+                     p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta,
+                     (__bf16*)dq, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask, nqb, BH);
   return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t launch_m(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                    const float* delta, void* dq) {
+  const bool pad = p.seqlens != nullptr;
+  if (p.causal)
+    return pad ? launch<D, true, true, SPARSE>(p, q, k, v, dO, lse2, delta, dq)
+               : launch<D, true, false, SPARSE>(p, q, k, v, dO, lse2, delta, dq);
+  return pad ? launch<D, false, true, SPARSE>(p, q, k, v, dO, lse2, delta, dq)
+             : launch<D, false, false, SPARSE>(p, q, k, v, dO, lse2, delta, dq);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                     const float* delta, void* dq) {
-  const bool pad = p.seqlens != nullptr;
-  if (p.causal)
-    return pad ? launch<D, true, true>(p, q, k, v, dO, lse2, delta, dq) : launch<D, true, false>(p, q, k, v, dO, lse2, delta, dq);
-  return pad ? launch<D, false, true>(p, q, k, v, dO, lse2, delta, dq) : launch<D, false, false>(p, q, k, v, dO, lse2, delta, dq);
+  return p.block_mask != nullptr ? launch_m<D, true>(p, q, k, v, dO, lse2, delta, dq)
+                                 : launch_m<D, false>(p, q, k, v, dO, lse2, delta, dq);
 }
 
 }  // namespace

@@ -232,4 +232,53 @@ __device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
   return L < 0 ? 0 : (L > N ? N : L);
 }
 
+// ---- block-sparse attention: the visible tiles of a workgroup, compacted into an LDS list
+//
+// The block mask has 128 x 128 blocks; a kernel tile (a run of keys or of queries) never straddles
+// two blocks.  For a run of blocks [b0, b1) of one mask row or column, flags(b) is nonzero when block
+// b is visible (its low bits may carry per-wave visibility), and each visible block contributes its
+// tiles [b TPB, min((b + 1) TPB, tile_end)), b1 = ceil(tile_end / TPB).  Entries are
+// tile | flags << 12, in increasing tile order; the tile count goes to *count.  One whole wave runs
+// it; the caller synchronises before the list is read.
+constexpr int kMaskBlock = 128;       // rows and columns of one mask block
+constexpr int kMaxMaskBlocks = 1024;  // blocks per side of the largest block mask (N <= 131072)
+constexpr int kTileBits = 12;         // tile index bits of a list entry
+
+template <int TPB, class Flags>
+__device__ __forceinline__ void compact_tiles(FA_LDS uint16_t* list, FA_LDS int* count, int b0, int b1, int tile_end,
+                                              Flags flags) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;  // visible blocks so far (wave-uniform)
+  for (int c = b0; c < b1; c += 64) {
+    const int blk = c + lane;
+    const int f = blk < b1 ? flags(blk) : 0;
+    const uint64_t m = __ballot(f != 0);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (f != 0) {
+#pragma unroll
+      for (int i = 0; i < TPB; ++i) {
+        const int tile = blk * TPB + i;
+        if (tile < tile_end) list[(total + rank) * TPB + i] = (uint16_t)(tile | (f << kTileBits));
+      }
+    }
+    total += __popcll(m);
+  }
+  const int last = b1 > b0 ? flags(b1 - 1) : 0;  // the last block may hold fewer than TPB tiles
+  if (lane == 0) *count = total * TPB - (last != 0 ? b1 * TPB - tile_end : 0);
+}
+
+__device__ __forceinline__ int list_tile(uint16_t e) { return e & ((1 << kTileBits) - 1); }
+__device__ __forceinline__ int list_flags(uint16_t e) { return e >> kTileBits; }
+
+// Number of list entries whose tile is below x (the list is sorted by tile).
+__device__ __forceinline__ int count_below(const FA_LDS uint16_t* list, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list_tile(list[mid]) < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace fa

@@ -21,6 +21,15 @@ __device__ __forceinline__ bool visible(int query, int key, int L) {
   return key < L && (!CAUSAL || key <= query);
 }
 
+// Block-sparse: whether mask block (query row r, key column c) of head bh is visible (always, when
+// there is no block mask).  Workgroups (64 rows) and tiles (32 rows) never straddle a 128 x 128
+// block, so one lookup decides a whole tile for the whole workgroup.
+__device__ __forceinline__ bool block_visible(const uint8_t* bmask, int64_t bh, int N, int r, int c) {
+  if (bmask == nullptr) return true;
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  return bmask[(bh * nb + r / kMaskBlock) * nb + c / kMaskBlock] != 0;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Forward: thread = query row; K/V tiles of 32 keys in LDS; per tile the 32 scores are formed,
 // the running max/normaliser updated once, and the output rescaled once.
@@ -28,7 +37,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, float* __restrict__ O,
                                                      float* __restrict__ LSE, int H, int N, float scale,
-                                                     const int32_t* __restrict__ seqlens) {
+                                                     const int32_t* __restrict__ seqlens,
+                                                     const uint8_t* __restrict__ bmask) {
   __shared__ float ks[kF32Tile][D];
   __shared__ float vs[kF32Tile][D];
   const int h = blockIdx.y, b = blockIdx.z;
@@ -47,6 +57,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   int kend = L;
   if (CAUSAL) kend = min(kend, q0 + kF32Rows);
   for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+    if (!block_visible(bmask, (int64_t)b * H + h, N, q0, k0)) continue;
     __syncthreads();
     for (int i = threadIdx.x; i < kF32Tile * D; i += 64) {
       const int r = i / D, c = i % D;
@@ -96,7 +107,8 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ V, const float* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                                         float* __restrict__ dK, float* __restrict__ dV, int H, int N,
-                                                        float scale, const int32_t* __restrict__ seqlens) {
+                                                        float scale, const int32_t* __restrict__ seqlens,
+                                                        const uint8_t* __restrict__ bmask) {
   __shared__ float kr[kF32Rows][D + 1];
   __shared__ float vr[kF32Rows][D + 1];
   __shared__ float qs[kF32Tile][D];
@@ -122,6 +134,7 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict_
   const int qstart = CAUSAL ? k0 : 0;
   const int qtile0 = (k0 < L) ? (qstart / kF32Tile) * kF32Tile : N;  // no visible key: skip the walk
   for (int qt0 = qtile0; qt0 < N; qt0 += kF32Tile) {
+    if (!block_visible(bmask, (int64_t)b * H + h, N, qt0, k0)) continue;
     __syncthreads();
     for (int i = threadIdx.x; i < kF32Tile * D; i += 64) {
       const int r = i / D, c = i % D;
@@ -169,7 +182,8 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                                        float* __restrict__ dQ, int H, int N, float scale,
-                                                       const int32_t* __restrict__ seqlens) {
+                                                       const int32_t* __restrict__ seqlens,
+                                                       const uint8_t* __restrict__ bmask) {
   __shared__ float qr[kF32Rows][D + 1];
   __shared__ float gr[kF32Rows][D + 1];
   __shared__ float ks[kF32Tile][D];
@@ -194,6 +208,7 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
   int kend = L;
   if (CAUSAL) kend = min(kend, q0 + kF32Rows);
   for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+    if (!block_visible(bmask, (int64_t)b * H + h, N, q0, k0)) continue;
     __syncthreads();
     for (int i = threadIdx.x; i < kF32Tile * D; i += 64) {
       const int r = i / D, c = i % D;
@@ -226,7 +241,7 @@ template <int D, bool CAUSAL>
 hipError_t fwd(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, o, lse, p.H, p.N, p.scale,
-                     p.seqlens);
+                     p.seqlens, p.block_mask);
   return hipGetLastError();
 }
 
@@ -235,7 +250,7 @@ hipError_t bwd_kv(const Problem& p, const float* q, const float* k, const float*
                   const float* delta, float* dk, float* dv) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dk, dv,
-                     p.H, p.N, p.scale, p.seqlens);
+                     p.H, p.N, p.scale, p.seqlens, p.block_mask);
   return hipGetLastError();
 }
 
@@ -244,7 +259,7 @@ hipError_t bwd_q(const Problem& p, const float* q, const float* k, const float* 
                  const float* delta, float* dq) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dq, p.H,
-                     p.N, p.scale, p.seqlens);
+                     p.N, p.scale, p.seqlens, p.block_mask);
   return hipGetLastError();
 }
 

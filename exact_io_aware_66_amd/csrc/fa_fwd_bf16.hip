@@ -35,8 +35,12 @@
 //     head's K/V stays in that XCD's L2.
 #include <type_traits>
 
+#include "fa.h"
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+
+static_assert(fa::kMaskBlock == FA_MASK_BLOCK && fa::kMaskBlock * fa::kMaxMaskBlocks == FA_MASK_MAX_N,
+              "block-mask geometry of the kernels and of the C ABI agree");
 
 namespace fa {
 namespace {
@@ -47,11 +51,12 @@ constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 128 query rows per workg
 constexpr int kFwdBc = 64;                           // keys per tile
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG>
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
-                                                          const int32_t* __restrict__ seqlens, int nqb, int BH) {
+                                                          const int32_t* __restrict__ seqlens,
+                                                          const uint8_t* __restrict__ bmask, int nqb, int BH) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = kFwdBc * D * 2;      // bytes of one K or V tile
   constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
@@ -65,6 +70,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
   FA_LDS char* const kbuf[2] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw};
   FA_LDS char* const vbuf[2] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw};
+  // block-sparse: the visible key tiles of this query block, in order (two per mask block)
+  __shared__ uint16_t tlist_raw[SPARSE ? 2 * kMaxMaskBlocks : 1];
+  __shared__ int tcount_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -95,12 +103,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   const int qw = q0 + wave * kFwdRowsPerWave;
   const int query = qw + l32;
   const int kv_end = CAUSAL ? min(L, q0 + kFwdBr) : L;
-  const int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;  // tiles the workgroup loads
+  int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;  // tiles the workgroup loads
   const int wave_end = CAUSAL ? min(L, qw + kFwdRowsPerWave) : L;
-  const int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes (>= 1 when L > 0)
-  int n_full = L / kFwdBc;                              // leading tiles with no hidden pair
+  int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes (>= 1 when L > 0)
+  int n_full = L / kFwdBc;                        // leading tiles with no hidden pair
   if (CAUSAL) n_full = min(n_full, qw / kFwdBc);
-  const int n_clean = min(n_full, n_wave);
+  int n_clean = min(n_full, n_wave);
+  // Block-sparse: the loop below walks the list of visible tiles instead of tiles 0 .. ntiles-1; the
+  // counts become positions in that list (the list is in tile order, so the fully visible tiles are
+  // still its head).  A tile is always wholly inside one mask block.
+  const FA_LDS uint16_t* const tlist = (const FA_LDS uint16_t*)tlist_raw;
+  if constexpr (SPARSE) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const uint8_t* brow = bmask + ((int64_t)bh * nb + qblock) * nb;
+    if (wave == 0)
+      compact_tiles<kMaskBlock / kFwdBc>((FA_LDS uint16_t*)tlist_raw, (FA_LDS int*)&tcount_raw, 0,
+                                         (ntiles + 1) / 2, ntiles, [&](int kb) { return brow[kb] != 0 ? 1 : 0; });
+    __syncthreads();
+    const int n = *(volatile FA_LDS int*)&tcount_raw;
+    n_wave = count_below(tlist, n, n_wave);
+    n_clean = count_below(tlist, n, n_clean);
+    ntiles = n;
+  }
+  // position t of the walk -> key tile
+  auto tix = [&](int t) { return SPARSE ? list_tile(tlist[t]) : t; };
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds query `query`, d = 16 ds + 8 half .. +7
   bf16x8 qf[DS];
@@ -133,6 +159,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     voff[n] = (uint32_t)(r * D + 8 * c) * 2;
   }
   auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
+    t = tix(t);
     const u32x4 rs = make_rsrc(src + (int64_t)t * kFwdBc * D, (N - t * kFwdBc) * D * 2);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kFwdWaves + wave) * 1024);
@@ -223,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   // scaled to the base-2 domain in place; raise the maximum to the tile's.  Returns the factor O and
   // l must be multiplied by (1 when the maximum is unchanged).
   auto mask_update = [&](int set, int t) -> float {
-    const int key0 = t * kFwdBc;
+    const int key0 = tix(t) * kFwdBc;
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -427,28 +454,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG>
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const int nqb = (p.N + kFwdBr - 1) / kFwdBr;
   const int BH = p.B * p.H;
   const float c_log2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2,
-                     p.seqlens, nqb, BH);
+                     p.seqlens, p.block_mask, nqb, BH);
   return hipGetLastError();
 }
 
-template <int D, bool NEG>
+template <int D, bool NEG, bool SPARSE>
 hipError_t launch_mask(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const bool pad = p.seqlens != nullptr;
   if (p.causal)
-    return pad ? launch<D, true, true, NEG>(p, q, k, v, o, lse) : launch<D, true, false, NEG>(p, q, k, v, o, lse);
-  return pad ? launch<D, false, true, NEG>(p, q, k, v, o, lse) : launch<D, false, false, NEG>(p, q, k, v, o, lse);
+    return pad ? launch<D, true, true, NEG, SPARSE>(p, q, k, v, o, lse) : launch<D, true, false, NEG, SPARSE>(p, q, k, v, o, lse);
+  return pad ? launch<D, false, true, NEG, SPARSE>(p, q, k, v, o, lse) : launch<D, false, false, NEG, SPARSE>(p, q, k, v, o, lse);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
-  return p.scale < 0.f ? launch_mask<D, true>(p, q, k, v, o, lse) : launch_mask<D, false>(p, q, k, v, o, lse);
+  if (p.block_mask != nullptr)
+    return p.scale < 0.f ? launch_mask<D, true, true>(p, q, k, v, o, lse) : launch_mask<D, false, true>(p, q, k, v, o, lse);
+  return p.scale < 0.f ? launch_mask<D, true, false>(p, q, k, v, o, lse) : launch_mask<D, false, false>(p, q, k, v, o, lse);
 }
 
 }  // namespace

@@ -14,6 +14,7 @@ struct Problem {
   bool causal;
   const int32_t* seqlens;  // device int32[B] or nullptr
   hipStream_t stream;
+  const uint8_t* block_mask = nullptr;  // device uint8[B][H][nb][nb] (nb = ceil(N/128)), or nullptr: dense
 };
 
 // Workspace carve-up of the backward (byte offsets; all 256-byte aligned).

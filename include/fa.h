@@ -124,6 +124,36 @@ fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const vo
                            const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * Block-sparse attention: the computation above restricted to a pattern of 128 x 128 blocks.
+ * The pages describe the block-sparse extension as the same tiling applied to a sparse attention
+ * pattern ("FlashAttention: The IO-Aware Algorithm That Rewrote GPU Training Speed Records",
+ * promptingindex page, section "Benchmark results: speed records without any approximation";
+ * NOTE-005: FlashAttention, "Key components" and "Limitations", where it is approximate relative
+ * to dense attention).  Relative to its own mask the result is exact.
+ *   block_mask : device uint8 array [B][H][nb][nb], nb = ceil(N / FA_MASK_BLOCK), row-major and
+ *                contiguous, caller-owned, read only.  Entry (qb, kb) != 0 makes key j visible to
+ *                query i when i / FA_MASK_BLOCK == qb and j / FA_MASK_BLOCK == kb; the causal and
+ *                seqlens masks still apply (AND).  Blocks that are zero are skipped: their key or
+ *                query tiles are neither loaded nor computed.  A row with no visible key gets O = 0,
+ *                LSE = -inf and no gradient.
+ *   N must be at most FA_MASK_MAX_N (FA_ERR_UNSUPPORTED otherwise); block_mask must not be NULL.
+ * All other arguments, layouts, ownership and errors are those of fa_forward and fa_backward
+ * (same workspace size); fa_backward_block_sparse must receive the o and lse that
+ * fa_forward_block_sparse produced with the same block mask.
+ */
+#define FA_MASK_BLOCK 128
+#define FA_MASK_MAX_N 131072
+fa_status_t fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int H, int N, int d, float scale, int causal,
+                                    const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype,
+                                    void* stream);
+fa_status_t fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                     int B, int H, int N, int d, float scale, int causal,
+                                     const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

@@ -41,14 +41,17 @@ def rel_rms(got, ref):
 
 
 def run_gpu(fa, x, backward=True, dev="cuda"):
-    """Forward (and backward) of the HIP path on the inputs dict from workloads.draw*."""
+    """Forward (and backward) of the HIP path on the inputs dict from workloads.draw* (with
+    x["block_mask"], the block-sparse entry points)."""
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     sl = x.get("seqlens")
     sl = None if sl is None else sl.to(dev)
-    o, lse = fa.forward(q, k, v, x["scale"], x["causal"], sl)
+    bm = x.get("block_mask")
+    bm = None if bm is None else bm.to(dev)
+    o, lse = fa.forward(q, k, v, x["scale"], x["causal"], sl, block_mask=bm)
     out = {"o": o, "lse": lse}
     if backward:
-        dq, dk, dv = fa.backward(q, k, v, o, do, lse, x["scale"], x["causal"], sl)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, x["scale"], x["causal"], sl, block_mask=bm)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in out.items()}

@@ -103,3 +103,40 @@ def test_python_binding_rejects_unsupported_dtype_without_fallback():
     with pytest.raises(fa.FAError) as ei:
         fa._dtype_code(q)
     assert ei.value.status == UNSUPPORTED
+
+
+def _fwd_bs(lib, block_mask=P + 40960, N=300, **kw):
+    a = dict(q=P, k=P + 4096, v=P + 8192, o=P + 12288, lse=P + 16384, B=2, H=3, d=64, scale=0.125, causal=0,
+             seqlens=None, dtype=BF16)
+    a.update(kw)
+    return lib.fa_forward_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], N, a["d"], a["scale"],
+                                       a["causal"], a["seqlens"], block_mask, a["dtype"], None)
+
+
+def _bwd_bs(lib, block_mask=P + 40960, N=300, ws_bytes=None):
+    ws_bytes = lib.fa_backward_workspace_size(2, 3, N, 64, BF16) if ws_bytes is None else ws_bytes
+    return lib.fa_backward_block_sparse(P, P + 4096, P + 8192, P + 12288, P + 24576, P + 16384, P + 20480, P + 28672,
+                                        P + 32768, 2, 3, N, 64, 0.125, 1, None, block_mask, BF16, P + 65536, ws_bytes,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_mask=None), INVALID), (dict(N=131073), UNSUPPORTED), (dict(q=None), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(lse=P + 2), MISALIGNED),
+])
+def test_block_sparse_forward_argument_errors(lib, kw, code):
+    assert _fwd_bs(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,code", [(dict(block_mask=None), INVALID), (dict(N=131073), UNSUPPORTED),
+                                     (dict(ws_bytes=8), WORKSPACE)])
+def test_block_sparse_backward_argument_errors(lib, kw, code):
+    assert _bwd_bs(lib, **kw) == code
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_block_sparse_valid_arguments_without_device_report_hip_error(lib):
+    assert _fwd_bs(lib) == HIP
+    assert _bwd_bs(lib) == HIP
+    assert _fwd_bs(lib, N=131072) == HIP  # the largest supported sequence
