@@ -168,6 +168,78 @@ def naive_torch_forward(w, x, steps: int):
     return a.elapsed_time(b) / steps
 
 
+def block_pairs(bm, N: int, causal: bool, lens) -> int:
+    """Visible (query, key) pairs of a [B, H, nb, nb] block mask combined with the causal mask and
+    the key lengths (per batch element)."""
+    import torch
+    B, H, nb, _ = bm.shape
+    blk = 128
+    qb = torch.arange(nb)[:, None].expand(nb, nb)
+    kb = torch.arange(nb)[None, :].expand(nb, nb)
+    total = 0
+    for b in range(B):
+        L = N if lens is None else max(0, min(N, int(lens[b])))
+        r0, r1 = qb * blk, torch.clamp((qb + 1) * blk, max=N)
+        k0, k1 = kb * blk, torch.clamp(torch.clamp((kb + 1) * blk, max=N), max=L)
+        rows = r1 - r0
+        if not causal:
+            per = rows * torch.clamp(k1 - k0, min=0)
+        else:  # sum over rows i of max(0, min(k1, i + 1) - k0)
+            per = torch.zeros(nb, nb, dtype=torch.int64)
+            for off in range(blk):
+                i = r0 + off
+                per += torch.where(i < r1, torch.clamp(torch.minimum(k1, i + 1) - k0, min=0), 0)
+        total += int((per * (bm[b] != 0).to(torch.int64)).sum())
+    return total
+
+
+def measure_block_sparse(fa, w, x, pattern: str, steps: int, dense_ms: tuple):
+    """Forward and backward of workload w with a block mask (fa_forward_block_sparse,
+    fa_backward_block_sparse): time per step, FLOPs over the visible pairs only, speedup over the
+    dense steps."""
+    import torch
+
+    import workloads
+    dev = torch.device("cuda:0")
+    bm = workloads.draw_block_mask(w.B, w.H, w.N, pattern, density=0.5, window=1, seed=7)
+    pairs = block_pairs(bm, w.N, w.causal, x["seqlens"])
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    sl = None if x["seqlens"] is None else x["seqlens"].to(dev)
+    bmd = bm.to(dev)
+    o, lse = torch.empty_like(q), torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def fwd():
+        fa.fa_forward_block_sparse(q, k, v, o, lse, x["scale"], w.causal, sl, bmd)
+
+    def bwd():
+        fa.fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, x["scale"], w.causal, sl, bmd, ws)
+
+    for _ in range(5):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for _ in range(steps):
+        fwd()
+    e[1].record(stream)
+    for _ in range(steps):
+        bwd()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    ms_f, ms_b = e[0].elapsed_time(e[1]) / steps, e[1].elapsed_time(e[2]) / steps
+    ff = 4.0 * w.d * pairs
+    dense_pairs = workload_flops(w, x)[0] / (4.0 * w.d)
+    return {"pattern": pattern, "visible_blocks": int((bm != 0).sum()), "blocks": bm.numel(),
+            "visible_pairs_frac_of_dense": round(pairs / dense_pairs, 4),
+            "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "fwd_tflops": round(ff / (ms_f * 1e-3) / 1e12, 2), "fwd_bwd_tflops": round(3.5 * ff / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+            "speedup_vs_dense_fwd_bwd": round((dense_ms[0] + dense_ms[1]) / (ms_f + ms_b), 3)}
+
+
 def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = False):
     """Time `steps` fwd+bwd steps of workload w (inputs resident on the device): clock settling,
     warm-up, then HIP events around the timed region and around every launch."""
@@ -237,6 +309,8 @@ def main():
                     help="repeat the step untimed for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-sparse", action="store_true",
+                    help="skip the block-sparse measurements (same workload, two block masks)")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with a 512 MiB scratch write between them (cold caches)")
     ap.add_argument("--all-configs", action="store_true",
@@ -333,6 +407,9 @@ def main():
                      "traffic": measured_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                      "ms_per_launch": round(dom_ms, 4)},
     }
+    if not args.no_block_sparse:
+        out["block_sparse"] = [measure_block_sparse(fa, w, x, pat, args.steps, (ms_fwd, ms_bwd))
+                               for pat in ("local+global", "random")]
     if args.cold:
         rc = measure(fa, w, x, args.steps, args.warmup, 0.0, cold=True)
         out["cold"] = {"note": "512 MiB scratch written between steps (outside the timed kernels)",
