@@ -5,3 +5,4 @@ leg.  The product path never imports it.
 """
 from .attention import (backward, backward_keys, backward_rows, forward, forward_rows,  # noqa: F401
                         key_lengths, row_stats, visible, block_count, MASK_BLOCK)
+from .philox import dropout_keep, keep_threshold, philox4x32_10  # noqa: F401,E402

@@ -12,8 +12,11 @@ What it computes, and where that is defined
 * "FlashAttention: The IO-Aware Algorithm That Rewrote GPU Training Speed
   Records" (promptingindex.com), section "Why attention is memory-bound, not
   compute-bound": attention is the chain matmul -> scaling -> masking ->
-  softmax -> (dropout) -> matmul with V.  Dropout is not part of the path
-  built here (probability 0).
+  softmax -> (dropout) -> matmul with V.  Dropout is optional: ``forward`` and
+  ``backward`` take an explicit keep mask Z (bool [B, H, N, N]) and the scale s
+  of the kept probabilities (oracle/philox.py builds Z from a seed; the kernels
+  regenerate the same mask themselves).  The dropped attention is
+  O = (P * Z s) V; LSE stays that of the undropped P;
 * The same NOTE-005 page, "Method": the forward keeps a running max m and a
   normaliser l per row and the backward recomputes the attention block from
   them.  The quantity stored per row is LSE = m + ln l, the natural-log
@@ -43,7 +46,9 @@ Readings where the pages are silent (each is also listed in the design doc):
 * backward of the loss sum(dO * O): dV = Pᵀ dO, dP = dO Vᵀ,
   D_i = sum_j P_ij dP_ij, dS = P * (dP - D), dQ = scale * dS K,
   dK = scale * dSᵀ Q -- the chain rule through the definition above (the pages
-  only say that the backward recomputes the block).
+  only say that the backward recomputes the block).  With dropout the chain
+  passes through P * Z s: dV = (P Z s)ᵀ dO, dP = (dO Vᵀ) Z s, and D_i, dS, dQ, dK
+  as above (D_i = sum_j P_ij dP_ij = dO_i . O_i still holds).
 
 Inputs may be any floating dtype; they are promoted exactly to float64, so the
 oracle sees the stored (e.g. bfloat16) values themselves.
@@ -134,7 +139,12 @@ def _probs(s, lse):
     return torch.where(empty[:, None], torch.zeros_like(p), p)
 
 
-def forward(q, k, v, scale: float, causal: bool = False, seqlens=None, block_mask=None):
+def _keep(keep, b, h):
+    return None if keep is None else torch.as_tensor(keep)[b, h].to("cpu")
+
+
+def forward(q, k, v, scale: float, causal: bool = False, seqlens=None, block_mask=None, keep=None,
+            keep_scale: float = 1.0):
     """O and LSE for [B, H, N, d] inputs; returns fp64 tensors O [B,H,N,d] and LSE [B,H,N].
 
     NOTE-005 "Key results" Theorem 1 (O = softmax(QKᵀ)V) with the scaling and
@@ -155,11 +165,15 @@ def forward(q, k, v, scale: float, causal: bool = False, seqlens=None, block_mas
             s = _scores(q[b, h], k[b, h], scale, vis)
             lse[b, h] = _row_lse(s)
             p = _probs(s, lse[b, h])
+            z = _keep(keep, b, h)
+            if z is not None:
+                p = torch.where(z, p * float(keep_scale), torch.zeros_like(p))
             o[b, h] = torch.matmul(p, v[b, h])
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None, block_mask=None):
+def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None, block_mask=None, keep=None,
+             keep_scale: float = 1.0):
     """dQ, dK, dV (fp64) of the loss sum(dO * O) through the definition of ``forward``.
 
     The pages state only that the backward recomputes the attention block from
@@ -182,8 +196,12 @@ def backward(q, k, v, do, scale: float, causal: bool = False, seqlens=None, bloc
             vis = vis_b if blocks is None else visible(N, causal, L[b], blocks=blocks)
             s = _scores(q[b, h], k[b, h], scale, vis)
             p = _probs(s, _row_lse(s))
-            dv[b, h] = torch.matmul(p.transpose(0, 1), do[b, h])
+            z = _keep(keep, b, h)
+            pz = p if z is None else torch.where(z, p * float(keep_scale), torch.zeros_like(p))
+            dv[b, h] = torch.matmul(pz.transpose(0, 1), do[b, h])
             dp = torch.matmul(do[b, h], v[b, h].transpose(0, 1))
+            if z is not None:
+                dp = torch.where(z, dp * float(keep_scale), torch.zeros_like(dp))
             D = torch.sum(p * dp, dim=1, keepdim=True)
             ds = p * (dp - D)
             dq[b, h] = torch.matmul(ds, k[b, h]) * scale

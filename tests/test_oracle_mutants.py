@@ -29,7 +29,7 @@ MUTANTS = [
     ("drop scale in dQ", "dq[b, h] = torch.matmul(ds, k[b, h]) * scale", "dq[b, h] = torch.matmul(ds, k[b, h])"),
     ("transpose dS in dK", "dk[b, h] = torch.matmul(ds.transpose(0, 1), q[b, h]) * scale",
      "dk[b, h] = torch.matmul(ds, q[b, h]) * scale"),
-    ("transpose P in dV", "dv[b, h] = torch.matmul(p.transpose(0, 1), do[b, h])", "dv[b, h] = torch.matmul(p, do[b, h])"),
+    ("transpose P in dV", "dv[b, h] = torch.matmul(pz.transpose(0, 1), do[b, h])", "dv[b, h] = torch.matmul(pz, do[b, h])"),
     ("wrong D in row stats", "D[rows] = torch.sum(o_r * doh[rows], dim=1)", "D[rows] = torch.sum(o_r, dim=1)"),
     ("drop D in column view", "ds = p * (dp - _f64(D)[:, None])", "ds = p * dp"),
     ("dP uses Q in row view", "dp = torch.matmul(doh[rows], vh.transpose(0, 1))",
