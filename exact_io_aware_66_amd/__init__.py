@@ -8,6 +8,9 @@ missing or a call is unsupported, these functions raise.
     fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace)
     fa_backward_workspace_size(B, H, N, d, dtype)
     fa_forward_block_sparse(q, k, v, o, lse, scale, causal, seqlens, block_mask)
+    fa_forward_dropout(q, k, v, o, lse, scale, causal, seqlens, p, seed, offset)
+    fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, p, seed, offset, workspace)
+    fa_dropout_mask(B, H, N, p, seed, offset, keep)
     fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace)
     forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
     backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
@@ -28,8 +31,8 @@ FA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_MISALIGNED",
           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
-           "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_status_string",
-           "fa_last_error")
+           "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
+           "fa_backward_dropout", "fa_dropout_mask", "fa_status_string", "fa_last_error")
 MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
 
 _lib = None
@@ -64,6 +67,14 @@ def load(path: str = LIB_PATH):
     lib.fa_forward_block_sparse.restype = i
     lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
     lib.fa_backward_block_sparse.restype = i
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, u32, i, vp]
+    lib.fa_forward_dropout.restype = i
+    lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, u32, i, vp, sz,
+                                        vp]
+    lib.fa_backward_dropout.restype = i
+    lib.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
+    lib.fa_dropout_mask.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -186,6 +197,39 @@ def fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale: float, caus
                                         _ptr(block_mask), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
 
 
+def fa_forward_dropout(q, k, v, o, lse, scale: float, causal: bool, seqlens, p: float, seed: int, offset: int,
+                       stream=None) -> None:
+    """C-ABI fa_forward_dropout: dropout probability p, Philox seed (64-bit) and offset (32-bit)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, lse)
+    seqlens = _seqlens(seqlens, B, q.device)
+    _check(lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                  int(bool(causal)), _ptr(seqlens), float(p), int(seed), int(offset), _dtype_code(q),
+                                  _stream(stream)))
+
+
+def fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, seqlens, p: float, seed: int,
+                        offset: int, workspace, stream=None) -> None:
+    """C-ABI fa_backward_dropout (same p, seed and offset as the forward)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), float(p), int(seed),
+                                   int(offset), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_dropout_mask(B: int, H: int, N: int, p: float, seed: int, offset: int, keep, stream=None) -> None:
+    """C-ABI fa_dropout_mask into `keep`, a contiguous uint8 device tensor [B, H, N, N] (1 = kept)."""
+    lib = load()
+    if not (keep.is_cuda and keep.dtype == torch.uint8 and keep.is_contiguous() and tuple(keep.shape) == (B, H, N, N)):
+        raise ValueError("keep must be a contiguous uint8 device tensor [B, H, N, N]")
+    _check(lib.fa_dropout_mask(B, H, N, float(p), int(seed), int(offset), _ptr(keep), _stream(stream)))
+
+
 def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
     """Stage 1 of fa_backward: D = rowsum(dO * O) into the workspace (bf16: also LSE log2 e)."""
     lib = load()
@@ -225,13 +269,17 @@ def _default_scale(d: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
 
 
-def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=None, stream=None, block_mask=None):
-    """Allocate O and LSE and run fa_forward (fa_forward_block_sparse with a block mask); returns (o, lse)."""
+def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=None, stream=None, block_mask=None,
+            dropout=None):
+    """Allocate O and LSE and run fa_forward (fa_forward_block_sparse with a block mask, fa_forward_dropout
+    with dropout=(p, seed, offset)); returns (o, lse)."""
     B, H, N, d = _dims(q)
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if block_mask is None:
+    if dropout is not None:
+        fa_forward_dropout(q, k, v, o, lse, scale, causal, seqlens, *dropout, stream=stream)
+    elif block_mask is None:
         fa_forward(q, k, v, o, lse, scale, causal, seqlens, stream)
     else:
         fa_forward_block_sparse(q, k, v, o, lse, scale, causal, seqlens, block_mask, stream)
@@ -239,7 +287,7 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, seqlens=N
 
 
 def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, seqlens=None, stream=None,
-             workspace=None, block_mask=None):
+             workspace=None, block_mask=None, dropout=None):
     """Allocate dQ, dK, dV (and the workspace unless given) and run fa_backward (fa_backward_block_sparse
     with a block mask); returns (dq, dk, dv)."""
     B, H, N, d = _dims(q)
@@ -247,7 +295,9 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = Fal
     if workspace is None:
         workspace = torch.empty(fa_backward_workspace_size(B, H, N, d, q.dtype), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if block_mask is None:
+    if dropout is not None:
+        fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, *dropout, workspace, stream=stream)
+    elif block_mask is None:
         fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, workspace, stream)
     else:
         fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace,

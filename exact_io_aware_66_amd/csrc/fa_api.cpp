@@ -192,9 +192,34 @@ fa_status_t check_block_mask(const uint8_t* block_mask, int N) {
   return FA_OK;
 }
 
+// Dropout parameters of a call (none: p < 0 is never passed by the entry points that have no dropout).
+struct DropArgs {
+  bool on = false;
+  float p = 0.f;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
+};
+
+fa_status_t check_dropout(float p, int* t) {
+  if (!std::isfinite(p) || p < 0.f) return fail(FA_ERR_INVALID_ARGUMENT, "dropout_p must be finite and >= 0");
+  const double x = std::nearbyint((1.0 - (double)p) * 256.0);  // half to even
+  if (x < 1.0 || x > 256.0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "dropout_p=%g leaves no kept element (round((1-p)*256) < 1)", (double)p);
+  *t = (int)x;
+  return FA_OK;
+}
+
+void set_dropout(fa::Problem& pr, const DropArgs& dr, int t) {
+  pr.dropout = dr.on;
+  pr.drop_k0 = (uint32_t)dr.seed;
+  pr.drop_k1 = (uint32_t)(dr.seed >> 32);
+  pr.drop_off2 = 2u * dr.offset;
+  pr.drop_t = (uint32_t)t;
+}
+
 fa_status_t forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                          float scale, int causal, const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype,
-                         void* stream) {
+                         void* stream, const DropArgs& drop = DropArgs()) {
   fa_status_t s;
   if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
   if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
@@ -204,9 +229,12 @@ fa_status_t forward_impl(const void* q, const void* k, const void* v, void* o, f
   if (dtype == FA_DTYPE_BF16 && fa::fwd_bf16_grid(B, H, N) > 0x7fffffff)
     return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
   if ((s = check_head_bytes(N, d, dtype)) != FA_OK) return s;
+  int t = 256;
+  if (drop.on && (s = check_dropout(drop.p, &t)) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
   fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   p.block_mask = block_mask;
+  set_dropout(p, drop, t);
   const hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, q, k, v, o, lse)
                                : fa::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v, (float*)o, lse);
   if (e != hipSuccess) return hip_fail(e, "fa_forward launch");
@@ -216,15 +244,18 @@ fa_status_t forward_impl(const void* q, const void* k, const void* v, void* o, f
 fa_status_t backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                           const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, const DropArgs& drop = DropArgs()) {
   fa_status_t s;
   if ((s = validate_stage(q, k, v, dO, lse, {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}}, B, H, N, d, scale, seqlens, dtype,
                           workspace, workspace_bytes)) != FA_OK)
     return s;
   if ((s = check_tensor(o, "o")) != FA_OK) return s;
+  int t = 256;
+  if (drop.on && (s = check_dropout(drop.p, &t)) != FA_OK) return s;
   if ((s = check_device()) != FA_OK) return s;
   fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   p.block_mask = block_mask;
+  set_dropout(p, drop, t);
   if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
   if ((s = run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace)) != FA_OK) return s;
   return run_dq(p, dtype, q, k, v, dO, lse, dq, workspace);
@@ -256,6 +287,54 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
   g_last_error[0] = '\0';
   return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, nullptr, dtype, workspace,
                        workspace_bytes, stream);
+}
+
+fa_status_t fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                               int d, float scale, int causal, const int32_t* seqlens, float dropout_p, uint64_t seed,
+                               uint32_t offset, fa_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  DropArgs dr;
+  dr.on = true;
+  dr.p = dropout_p;
+  dr.seed = seed;
+  dr.offset = offset;
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, nullptr, dtype, stream, dr);
+}
+
+fa_status_t fa_backward_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                                int causal, const int32_t* seqlens, float dropout_p, uint64_t seed, uint32_t offset,
+                                fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  DropArgs dr;
+  dr.on = true;
+  dr.p = dropout_p;
+  dr.seed = seed;
+  dr.offset = offset;
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, nullptr, dtype, workspace,
+                       workspace_bytes, stream, dr);
+}
+
+fa_status_t fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset, uint8_t* keep,
+                            void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if (B <= 0 || H <= 0 || N <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "B, H and N must be positive (got %d, %d, %d)", B, H, N);
+  if (keep == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "keep is NULL");
+  const int64_t total = (int64_t)B * H * N * ((N + 31) / 32);
+  if ((total + 255) / 256 > 0x7fffffff) return fail(FA_ERR_INVALID_ARGUMENT, "B*H*N*ceil(N/32) too large");
+  int t = 256;
+  if ((s = check_dropout(dropout_p, &t)) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::Problem p = problem(B, H, N, 64, 1.f, 0, nullptr, stream);
+  DropArgs dr;
+  dr.on = true;
+  dr.p = dropout_p;
+  dr.seed = seed;
+  dr.offset = offset;
+  set_dropout(p, dr, t);
+  const hipError_t e = fa::launch_dropout_mask(p, keep);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "fa_dropout_mask launch");
 }
 
 fa_status_t fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO,

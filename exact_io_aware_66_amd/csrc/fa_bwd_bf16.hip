@@ -77,14 +77,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 template <int D>
 constexpr int bwd_rows_per_tile() { return D == 128 ? 32 : 64; }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                           const float* __restrict__ LSE2,
                                                           const float* __restrict__ DELTA, __bf16* __restrict__ dK,
                                                           __bf16* __restrict__ dV, int H, int N, float scale,
                                                           float c_log2, const int32_t* __restrict__ seqlens,
-                                                          const uint8_t* __restrict__ bmask, int BH) {
+                                                          const uint8_t* __restrict__ bmask, Dropout dr, int BH) {
   constexpr int BR = bwd_rows_per_tile<D>();  // query rows per tile
   constexpr int QS = BR / 32;                 // 32-row halves of a tile
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -106,6 +106,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   // block-sparse: the visible query tiles of this key block, in order (kBwdBc / BR per mask block)
   __shared__ uint16_t tlist_raw[SPARSE ? (kBwdBc / BR) * kMaxMaskBlocks : 1];
   __shared__ int tcount_raw;
+  // dropout: per wave, the keep bytes of each 32 x 32 (query, key) block of a tile, key-major
+  __shared__ __attribute__((aligned(16))) uint8_t drop_raw[DROP ? kBwdWaves * QS * 1024 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -258,6 +260,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       barrier();
       if (u + 3 < count) load_tile(u + 3, ldst);
 
+      // Dropout keep words of tile u in this kernel's layout (lane = key, 16 queries per 32-row half):
+      // each lane draws the words of one query (the layout the generator is defined in), writes the
+      // bytes key-major into the wave's LDS block and reads back the 4 words of its own key.
+      u32x4 kwt[QS];
+      if constexpr (DROP) {
+        const int qb0 = (SPARSE ? list_tile(tlist[u]) : it0 + u) * BR;
+        FA_LDS uint8_t* mt = (FA_LDS uint8_t*)drop_raw + wave * QS * 1024;
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          const u32x4 w = dropout_words(dr, (uint32_t)bh, qb0 + 32 * qs + l32, kw / 32, half);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mt[qs * 1024 + (8 * g + 4 * half + e) * 32 + l32] = (uint8_t)(w[g] >> (8 * e));
+        }
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) kwt[qs][g] = *(const FA_LDS uint32_t*)(mt + qs * 1024 + l32 * 32 + 8 * g + 4 * half);
+      }
+
       float cf = c_log2;
       if constexpr (MASK) {  // hidden pairs (key > query) to -inf, in the scaled domain
         const int qi0 = (it0 + u) * BR;
@@ -291,8 +314,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
           for (int h = 0; h < 2; ++h) {
             const int r = 8 * (ks & 1) + 2 * e + h;
             const float p = fast_exp2(fmaf(s[P][qs][r], cf, -lse4[qs][r >> 2][r & 3]));
-            s[P][qs][r] = p;
-            dp[P][qs][r] = p * (dp[P][qs][r] - del4[qs][r >> 2][r & 3]);
+            float dpv = dp[P][qs][r];
+            float pv = p;  // P for dV: the kept probabilities (their 256/t scale is applied to dV at the end)
+            if constexpr (DROP) {
+              const bool keep = ((kwt[qs][r >> 2] >> (8 * (r & 3))) & 0xFFu) < dr.t;
+              dpv = keep ? dpv * dr.scale : 0.f;
+              pv = keep ? p : 0.f;
+            }
+            s[P][qs][r] = pv;
+            dp[P][qs][r] = p * (dpv - del4[qs][r >> 2][r & 3]);
           }
         } else {
           pb[ks] = pack8(s[P][qs], 8 * (ks & 1));
@@ -403,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kx[e] = live ? dkt[dt][4 * gq + e] * scale : 0.f;
-          vx[e] = live ? dvt[dt][4 * gq + e] : 0.f;
+          vx[e] = live ? dvt[dt][4 * gq + e] * (DROP ? dr.scale : 1.f) : 0.f;
         }
         *(bf16x4*)(dkrow + d0) = pack4(kx[0], kx[1], kx[2], kx[3]);
         *(bf16x4*)(dvrow + d0) = pack4(vx[0], vx[1], vx[2], vx[3]);
@@ -411,33 +441,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
 hipError_t launch_dkdv(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                        const float* delta, void* dk, void* dv) {
   const int nkb = (p.N + kBwdBc - 1) / kBwdBc;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE>), dim3((unsigned)(nkb * BH)), dim3(256), 0, p.stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta, (__bf16*)dk,
-                     (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask, BH);
+  const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE, DROP>), dim3((unsigned)(nkb * BH)), dim3(256), 0,
+                     p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta,
+                     (__bf16*)dk, (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask, dr, BH);
   return hipGetLastError();
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool DROP>
 hipError_t launch_dkdv_m(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                          const float* lse2, const float* delta, void* dk, void* dv) {
   const bool pad = p.seqlens != nullptr;
   if (p.causal)
-    return pad ? launch_dkdv<D, true, true, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv)
-               : launch_dkdv<D, true, false, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv);
-  return pad ? launch_dkdv<D, false, true, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv)
-             : launch_dkdv<D, false, false, SPARSE>(p, q, k, v, dO, lse2, delta, dk, dv);
+    return pad ? launch_dkdv<D, true, true, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dk, dv)
+               : launch_dkdv<D, true, false, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dk, dv);
+  return pad ? launch_dkdv<D, false, true, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dk, dv)
+             : launch_dkdv<D, false, false, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dk, dv);
 }
 
 template <int D>
 hipError_t launch_dkdv_d(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                          const float* lse2, const float* delta, void* dk, void* dv) {
-  return p.block_mask != nullptr ? launch_dkdv_m<D, true>(p, q, k, v, dO, lse2, delta, dk, dv)
-                                 : launch_dkdv_m<D, false>(p, q, k, v, dO, lse2, delta, dk, dv);
+  if (p.dropout) return launch_dkdv_m<D, false, true>(p, q, k, v, dO, lse2, delta, dk, dv);
+  return p.block_mask != nullptr ? launch_dkdv_m<D, true, false>(p, q, k, v, dO, lse2, delta, dk, dv)
+                                 : launch_dkdv_m<D, false, false>(p, q, k, v, dO, lse2, delta, dk, dv);
 }
 
 template <int D, typename T>

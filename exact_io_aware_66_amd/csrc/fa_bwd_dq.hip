@@ -41,14 +41,15 @@ constexpr int kDqRowsPerWave = 32;
 constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // query rows per workgroup
 constexpr int kDqBc = 64;                         // keys per tile
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         const float* __restrict__ LSE2,
                                                         const float* __restrict__ DELTA, __bf16* __restrict__ dQ,
                                                         int H, int N, float scale, float c_log2,
                                                         const int32_t* __restrict__ seqlens,
-                                                        const uint8_t* __restrict__ bmask, int nqb, int BH) {
+                                                        const uint8_t* __restrict__ bmask, Dropout dr, int nqb,
+                                                        int BH) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kDqBc * D * 2;      // bytes of one K or V tile
   constexpr int LOADS = kDqBc * CH / (64 * kDqWaves);  // 16-byte loads per thread per tile
@@ -204,14 +205,20 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
       }
       cf = 1.f;
     }
+    // dropout: dP of the kept elements, scaled by 256/t; the others contribute P (0 - D)
+    u32x4 kwd = {};
+    if constexpr (DROP) kwd = dropout_words(dr, (uint32_t)bh, query, 2 * t + kt, half);
     bf16x8 dsb[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       float d8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(sv[8 * kh + e], cf, -lse2));
-        d8[e] = p * (dp[8 * kh + e] - del);
+        const int r = 8 * kh + e;
+        const float p = fast_exp2(fmaf(sv[r], cf, -lse2));
+        float dpv = dp[r];
+        if constexpr (DROP) dpv = dropout_keep(dr, kwd[r >> 2], r & 3) ? dpv * dr.scale : 0.f;
+        d8[e] = p * (dpv - del);
       }
       dsb[kh] = pack8f(d8, 0);
     }
@@ -297,33 +304,36 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                   const float* delta, void* dq) {
   const int nqb = (p.N + kDqBr - 1) / kDqBr;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE>), dim3((unsigned)(nqb * BH)), dim3(kDqWaves * 64), 0,
-                     p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, delta,
-                     (__bf16*)dq, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask, nqb, BH);
+  const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE, DROP>), dim3((unsigned)(nqb * BH)),
+                     dim3(kDqWaves * 64), 0, p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (const __bf16*)dO, lse2, delta, (__bf16*)dq, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens,
+                     p.block_mask, dr, nqb, BH);
   return hipGetLastError();
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool DROP>
 hipError_t launch_m(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                     const float* delta, void* dq) {
   const bool pad = p.seqlens != nullptr;
   if (p.causal)
-    return pad ? launch<D, true, true, SPARSE>(p, q, k, v, dO, lse2, delta, dq)
-               : launch<D, true, false, SPARSE>(p, q, k, v, dO, lse2, delta, dq);
-  return pad ? launch<D, false, true, SPARSE>(p, q, k, v, dO, lse2, delta, dq)
-             : launch<D, false, false, SPARSE>(p, q, k, v, dO, lse2, delta, dq);
+    return pad ? launch<D, true, true, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dq)
+               : launch<D, true, false, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dq);
+  return pad ? launch<D, false, true, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dq)
+             : launch<D, false, false, SPARSE, DROP>(p, q, k, v, dO, lse2, delta, dq);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                     const float* delta, void* dq) {
-  return p.block_mask != nullptr ? launch_m<D, true>(p, q, k, v, dO, lse2, delta, dq)
-                                 : launch_m<D, false>(p, q, k, v, dO, lse2, delta, dq);
+  if (p.dropout) return launch_m<D, false, true>(p, q, k, v, dO, lse2, delta, dq);
+  return p.block_mask != nullptr ? launch_m<D, true, false>(p, q, k, v, dO, lse2, delta, dq)
+                                 : launch_m<D, false, false>(p, q, k, v, dO, lse2, delta, dq);
 }
 
 }  // namespace

@@ -232,6 +232,48 @@ __device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
   return L < 0 ? 0 : (L > N ? N : L);
 }
 
+// ---- dropout: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+// 1, 2, 3", SC'11) and the keep decision of one (query, key) element.
+//
+// Element (bh, query i, key j) draws the byte of key j % 32 = 8 g + 4 h + e from output word g,
+// byte e, of Philox4x32-10 with counter (i, j / 32, bh, 2 offset + h) and key (seed low, seed high);
+// it is kept when that byte is below t = round((1 - p) 256), and kept probabilities are scaled by
+// 256 / t.  A lane that holds one query and the 16 keys 8 g + 4 h + e of a 32-key block (the score
+// layout of the forward and dQ kernels) needs exactly one call per block.
+struct Dropout {
+  uint32_t k0, k1;  // seed, low and high words
+  uint32_t off2;    // 2 offset
+  uint32_t t;       // keep threshold, 1..256
+  float scale;      // 256 / t
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The four keep words of (query i, 32-key block jb, half h): byte e of word g is key 8 g + 4 h + e.
+__device__ __forceinline__ u32x4 dropout_words(const Dropout& dr, uint32_t bh, int i, int jb, int h) {
+  return philox4x32_10((uint32_t)i, (uint32_t)jb, bh, dr.off2 + (uint32_t)h, dr.k0, dr.k1);
+}
+
+__device__ __forceinline__ bool dropout_keep(const Dropout& dr, uint32_t word, int e) {
+  return ((word >> (8 * e)) & 0xFFu) < dr.t;
+}
+
 // ---- block-sparse attention: the visible tiles of a workgroup, compacted into an LDS list
 //
 // The block mask has 128 x 128 blocks; a kernel tile (a run of keys or of queries) never straddles

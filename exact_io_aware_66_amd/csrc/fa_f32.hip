@@ -33,12 +33,12 @@ __device__ __forceinline__ bool block_visible(const uint8_t* bmask, int64_t bh, 
 // ---------------------------------------------------------------------------------------------
 // Forward: thread = query row; K/V tiles of 32 keys in LDS; per tile the 32 scores are formed,
 // the running max/normaliser updated once, and the output rescaled once.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, float* __restrict__ O,
                                                      float* __restrict__ LSE, int H, int N, float scale,
                                                      const int32_t* __restrict__ seqlens,
-                                                     const uint8_t* __restrict__ bmask) {
+                                                     const uint8_t* __restrict__ bmask, Dropout dr) {
   __shared__ float ks[kF32Tile][D];
   __shared__ float vs[kF32Tile][D];
   const int h = blockIdx.y, b = blockIdx.z;
@@ -66,6 +66,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
       vs[r][c] = V[(row0 + key) * D + c];
     }
     __syncthreads();
+    // dropout: keep words of this query for the tile's 32 keys (halves h = 0, 1)
+    u32x4 kw[2] = {};
+    if constexpr (DROP) {
+      kw[0] = dropout_words(dr, (uint32_t)(b * H + h), query, k0 / 32, 0);
+      kw[1] = dropout_words(dr, (uint32_t)(b * H + h), query, k0 / 32, 1);
+    }
     float s[kF32Tile];
     float tmax = -INFINITY;
 #pragma unroll
@@ -84,8 +90,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
     for (int c = 0; c < D; ++c) acc[c] *= alpha;
 #pragma unroll
     for (int j = 0; j < kF32Tile; ++j) {
-      const float p = expf(s[j] - m_use);
+      float p = expf(s[j] - m_use);
       l += p;
+      if constexpr (DROP) p = dropout_keep(dr, kw[(j >> 2) & 1][j >> 3], j & 3) ? p : 0.f;  // scaled at the end
 #pragma unroll
       for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vs[j][c], acc[c]);
     }
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   }
   if (query < N) {
     const bool has = l > 0.f;
-    const float inv = has ? 1.f / l : 0.f;
+    const float inv = has ? (DROP ? dr.scale : 1.f) / l : 0.f;
 #pragma unroll
     for (int c = 0; c < D; ++c) O[(row0 + query) * D + c] = acc[c] * inv;
     LSE[row0 + query] = has ? m + logf(l) : -INFINITY;
@@ -102,13 +109,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 
 // ---------------------------------------------------------------------------------------------
 // Backward, dK and dV: thread = key row (its K and V rows staged in LDS), loop over query tiles.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, const float* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                                         float* __restrict__ dK, float* __restrict__ dV, int H, int N,
                                                         float scale, const int32_t* __restrict__ seqlens,
-                                                        const uint8_t* __restrict__ bmask) {
+                                                        const uint8_t* __restrict__ bmask, Dropout dr) {
   __shared__ float kr[kF32Rows][D + 1];
   __shared__ float vr[kF32Rows][D + 1];
   __shared__ float qs[kF32Tile][D];
@@ -158,10 +165,17 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict_
         dp = fmaf(gs[i][c], vr[threadIdx.x][c], dp);
       }
       const float p = expf(s * scale - lse_s[i]);
+      float pz = p;  // dropout: the kept probability (scaled) feeds dV, the kept dP (scaled) feeds dS
+      if constexpr (DROP) {
+        const u32x4 w = dropout_words(dr, (uint32_t)(b * H + h), query, key / 32, (key >> 2) & 1);
+        const bool keep = dropout_keep(dr, w[(key & 31) >> 3], key & 3);
+        pz = keep ? p * dr.scale : 0.f;
+        dp = keep ? dp * dr.scale : 0.f;
+      }
       const float dsv = p * (dp - del_s[i]);
 #pragma unroll
       for (int c = 0; c < D; ++c) {
-        dv[c] = fmaf(p, gs[i][c], dv[c]);
+        dv[c] = fmaf(pz, gs[i][c], dv[c]);
         dk[c] = fmaf(dsv, qs[i][c], dk[c]);
       }
     }
@@ -177,13 +191,13 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict_
 
 // ---------------------------------------------------------------------------------------------
 // Backward, dQ: thread = query row (its Q and dO rows staged in LDS), loop over key tiles.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE, const float* __restrict__ DELTA,
                                                        float* __restrict__ dQ, int H, int N, float scale,
                                                        const int32_t* __restrict__ seqlens,
-                                                       const uint8_t* __restrict__ bmask) {
+                                                       const uint8_t* __restrict__ bmask, Dropout dr) {
   __shared__ float qr[kF32Rows][D + 1];
   __shared__ float gr[kF32Rows][D + 1];
   __shared__ float ks[kF32Tile][D];
@@ -217,6 +231,11 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
       vs[r][c] = V[(row0 + kk) * D + c];
     }
     __syncthreads();
+    u32x4 kw[2] = {};
+    if constexpr (DROP) {
+      kw[0] = dropout_words(dr, (uint32_t)(b * H + h), query, k0 / 32, 0);
+      kw[1] = dropout_words(dr, (uint32_t)(b * H + h), query, k0 / 32, 1);
+    }
     for (int j = 0; j < kF32Tile; ++j) {
       if (!visible<CAUSAL>(query, k0 + j, L)) continue;
       float s = 0.f, dp = 0.f;
@@ -226,6 +245,7 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
         dp = fmaf(gr[threadIdx.x][c], vs[j][c], dp);
       }
       const float p = expf(s * scale - lse);
+      if constexpr (DROP) dp = dropout_keep(dr, kw[(j >> 2) & 1][j >> 3], j & 3) ? dp * dr.scale : 0.f;
       const float dsv = p * (dp - del);
 #pragma unroll
       for (int c = 0; c < D; ++c) dq[c] = fmaf(dsv, ks[j][c], dq[c]);
@@ -237,37 +257,79 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
   }
 }
 
-template <int D, bool CAUSAL>
+Dropout dropout_of(const Problem& p) {
+  return Dropout{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
+}
+
+template <int D, bool CAUSAL, bool DROP>
 hipError_t fwd(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, o, lse, p.H, p.N, p.scale,
-                     p.seqlens, p.block_mask);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, DROP>), grid, dim3(64), 0, p.stream, q, k, v, o, lse, p.H, p.N, p.scale,
+                     p.seqlens, p.block_mask, dropout_of(p));
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t bwd_kv(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
                   const float* delta, float* dk, float* dv) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
-  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dk, dv,
-                     p.H, p.N, p.scale, p.seqlens, p.block_mask);
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL, DROP>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dk,
+                     dv, p.H, p.N, p.scale, p.seqlens, p.block_mask, dropout_of(p));
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t bwd_q(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
                  const float* delta, float* dq) {
   dim3 grid((p.N + kF32Rows - 1) / kF32Rows, p.H, p.B);
-  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dq, p.H,
-                     p.N, p.scale, p.seqlens, p.block_mask);
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL, DROP>), grid, dim3(64), 0, p.stream, q, k, v, dO, lse, delta, dq,
+                     p.H, p.N, p.scale, p.seqlens, p.block_mask, dropout_of(p));
   return hipGetLastError();
+}
+
+// Keep mask as bytes: one thread per (bh, query, 32-key block), both halves.
+__global__ __launch_bounds__(256) void dropout_mask_kernel(uint8_t* __restrict__ keep, int N, int64_t total,
+                                                           Dropout dr) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int nb32 = (N + 31) / 32;
+  const int jb = (int)(idx % nb32);
+  const int64_t rest = idx / nb32;
+  const int i = (int)(rest % N);
+  const int64_t bh = rest / N;
+  uint8_t* row = keep + (bh * N + i) * (int64_t)N;
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 w = dropout_words(dr, (uint32_t)bh, i, jb, h);
+    for (int g = 0; g < 4; ++g)
+      for (int e = 0; e < 4; ++e) {
+        const int j = 32 * jb + 8 * g + 4 * h + e;
+        if (j < N) row[j] = dropout_keep(dr, w[g], e) ? 1 : 0;
+      }
+  }
+}
+
+template <int D, bool DROP>
+hipError_t fwd_c(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse) {
+  return p.causal ? fwd<D, true, DROP>(p, q, k, v, o, lse) : fwd<D, false, DROP>(p, q, k, v, o, lse);
+}
+template <int D, bool DROP>
+hipError_t bwd_kv_c(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                    const float* delta, float* dk, float* dv) {
+  return p.causal ? bwd_kv<D, true, DROP>(p, q, k, v, dO, lse, delta, dk, dv)
+                  : bwd_kv<D, false, DROP>(p, q, k, v, dO, lse, delta, dk, dv);
+}
+template <int D, bool DROP>
+hipError_t bwd_q_c(const Problem& p, const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                   const float* delta, float* dq) {
+  return p.causal ? bwd_q<D, true, DROP>(p, q, k, v, dO, lse, delta, dq)
+                  : bwd_q<D, false, DROP>(p, q, k, v, dO, lse, delta, dq);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse) {
-  if (p.d == 64) return p.causal ? fwd<64, true>(p, q, k, v, o, lse) : fwd<64, false>(p, q, k, v, o, lse);
-  return p.causal ? fwd<128, true>(p, q, k, v, o, lse) : fwd<128, false>(p, q, k, v, o, lse);
+  if (p.d == 64) return p.dropout ? fwd_c<64, true>(p, q, k, v, o, lse) : fwd_c<64, false>(p, q, k, v, o, lse);
+  return p.dropout ? fwd_c<128, true>(p, q, k, v, o, lse) : fwd_c<128, false>(p, q, k, v, o, lse);
 }
 
 hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
@@ -275,10 +337,10 @@ hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k,
   const BwdWorkspace ws = bwd_workspace_layout(p.B, p.H, p.N, p.d, false);
   const float* delta = (const float*)((const char*)workspace + ws.delta_off);
   if (p.d == 64)
-    return p.causal ? bwd_kv<64, true>(p, q, k, v, dO, lse, delta, dk, dv)
-                    : bwd_kv<64, false>(p, q, k, v, dO, lse, delta, dk, dv);
-  return p.causal ? bwd_kv<128, true>(p, q, k, v, dO, lse, delta, dk, dv)
-                  : bwd_kv<128, false>(p, q, k, v, dO, lse, delta, dk, dv);
+    return p.dropout ? bwd_kv_c<64, true>(p, q, k, v, dO, lse, delta, dk, dv)
+                     : bwd_kv_c<64, false>(p, q, k, v, dO, lse, delta, dk, dv);
+  return p.dropout ? bwd_kv_c<128, true>(p, q, k, v, dO, lse, delta, dk, dv)
+                   : bwd_kv_c<128, false>(p, q, k, v, dO, lse, delta, dk, dv);
 }
 
 hipError_t launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
@@ -286,8 +348,15 @@ hipError_t launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, c
   const BwdWorkspace ws = bwd_workspace_layout(p.B, p.H, p.N, p.d, false);
   const float* delta = (const float*)((const char*)workspace + ws.delta_off);
   if (p.d == 64)
-    return p.causal ? bwd_q<64, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q<64, false>(p, q, k, v, dO, lse, delta, dq);
-  return p.causal ? bwd_q<128, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q<128, false>(p, q, k, v, dO, lse, delta, dq);
+    return p.dropout ? bwd_q_c<64, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q_c<64, false>(p, q, k, v, dO, lse, delta, dq);
+  return p.dropout ? bwd_q_c<128, true>(p, q, k, v, dO, lse, delta, dq) : bwd_q_c<128, false>(p, q, k, v, dO, lse, delta, dq);
+}
+
+hipError_t launch_dropout_mask(const Problem& p, uint8_t* keep) {
+  const int64_t total = (int64_t)p.B * p.H * p.N * ((p.N + 31) / 32);
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, p.stream, keep, p.N,
+                     total, dropout_of(p));
+  return hipGetLastError();
 }
 
 }  // namespace fa

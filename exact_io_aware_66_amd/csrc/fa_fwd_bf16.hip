@@ -51,12 +51,13 @@ constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 128 query rows per workg
 constexpr int kFwdBc = 64;                           // keys per tile
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens,
-                                                          const uint8_t* __restrict__ bmask, int nqb, int BH) {
+                                                          const uint8_t* __restrict__ bmask, Dropout dr, int nqb,
+                                                          int BH) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = kFwdBc * D * 2;      // bytes of one K or V tile
   constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
@@ -179,11 +180,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   //     pack and row sum (v_dot2_f32_bf16 on the packed values, so l sums exactly the weights used);
   //   xunit(set, u): four scores of the next tile into the running extreme ext (max, or min for a
   //     negative scale) for the lazy check.
+  // Dropout: keep words of the lane's query for the current tile's 32-key half kt (computed as a work
+  // unit before the P units that need them); l sums every probability, P V only the kept ones (the
+  // 256/t scale of the kept ones is applied to O in the epilogue).
+  u32x4 kwd = {};
+  auto dunit = [&](int t, int kt) {
+    if constexpr (DROP) kwd = dropout_words(dr, (uint32_t)bh, query, 2 * tix(t) + kt, half);
+  };
   auto punit = [&](int set, int ks, int e, float cf) {
     const int kt = ks >> 1, r = 8 * (ks & 1) + 2 * e;
     const f32x2 two = {fast_exp2(fmaf(s[set][kt][r], cf, -m_p)), fast_exp2(fmaf(s[set][kt][r + 1], cf, -m_p))};
     pk[ks][e] = __builtin_convertvector(two, bf16x2);
     l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[ks][e], ones, l_run, false);
+    if constexpr (DROP) {
+      const uint32_t w = kwd[r >> 2];
+      const f32x2 kept = {dropout_keep(dr, w, r & 3) ? two[0] : 0.f, dropout_keep(dr, w, (r & 3) + 1) ? two[1] : 0.f};
+      pk[ks][e] = __builtin_convertvector(kept, bf16x2);
+    }
     if (e == 3)
       pn[ks] = cat(__builtin_shufflevector(pk[ks][0], pk[ks][1], 0, 1, 2, 3),
                    __builtin_shufflevector(pk[ks][2], pk[ks][3], 0, 1, 2, 3));
@@ -334,7 +347,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
       auto ph1 = [&](int ds) {
 #pragma unroll
         for (int x = 0; x < 12; ++x)
-          if (x * DS / 12 == ds) punit(cur, x / 4, x % 4, cf);
+          if (x * DS / 12 == ds) {
+            if (x == 0) dunit(t, 0);
+            if (x == 8) dunit(t, 1);
+            punit(cur, x / 4, x % 4, cf);
+          }
       };
       if constexpr (NEXT != kNextNone) {
         scores(nxt, kbuf[nxt], ph1);
@@ -407,7 +424,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
       auto ph1 = [&](int ds) {
 #pragma unroll
         for (int x = 0; x < 12; ++x)
-          if (x * DS / 12 == ds) punit(0, x / 4, x % 4, cf);
+          if (x * DS / 12 == ds) {
+            if (x == 0) dunit(t, 0);
+            if (x == 8) dunit(t, 1);
+            punit(0, x / 4, x % 4, cf);
+          }
       };
       if constexpr (NEXT == kNextMasked) {
         scores(1, kb_nxt, ph1);
@@ -437,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   {
     const float l = add_halves(l_run);
     const bool has = l > 0.f;
-    const float inv = has ? 1.f / l : 0.f;
+    const float inv = has ? (DROP ? dr.scale : 1.f) / l : 0.f;
     if (query < N) {
       if (half == 0) LSE[row0 + query] = has ? (m_p + __log2f(l)) * kLn2 : -INFINITY;
       __bf16* orow = O + (row0 + query) * D;
@@ -454,30 +475,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE>
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const int nqb = (p.N + kFwdBr - 1) / kFwdBr;
   const int BH = p.B * p.H;
   const float c_log2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+  const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE, DROP>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2,
-                     p.seqlens, p.block_mask, nqb, BH);
+                     p.seqlens, p.block_mask, dr, nqb, BH);
   return hipGetLastError();
 }
 
-template <int D, bool NEG, bool SPARSE>
+template <int D, bool NEG, bool SPARSE, bool DROP>
 hipError_t launch_mask(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const bool pad = p.seqlens != nullptr;
   if (p.causal)
-    return pad ? launch<D, true, true, NEG, SPARSE>(p, q, k, v, o, lse) : launch<D, true, false, NEG, SPARSE>(p, q, k, v, o, lse);
-  return pad ? launch<D, false, true, NEG, SPARSE>(p, q, k, v, o, lse) : launch<D, false, false, NEG, SPARSE>(p, q, k, v, o, lse);
+    return pad ? launch<D, true, true, NEG, SPARSE, DROP>(p, q, k, v, o, lse)
+               : launch<D, true, false, NEG, SPARSE, DROP>(p, q, k, v, o, lse);
+  return pad ? launch<D, false, true, NEG, SPARSE, DROP>(p, q, k, v, o, lse)
+             : launch<D, false, false, NEG, SPARSE, DROP>(p, q, k, v, o, lse);
 }
 
 template <int D>
 hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
+  if (p.dropout)  // (dense attention only: the C ABI has no entry point that combines the two)
+    return p.scale < 0.f ? launch_mask<D, true, false, true>(p, q, k, v, o, lse)
+                         : launch_mask<D, false, false, true>(p, q, k, v, o, lse);
   if (p.block_mask != nullptr)
-    return p.scale < 0.f ? launch_mask<D, true, true>(p, q, k, v, o, lse) : launch_mask<D, false, true>(p, q, k, v, o, lse);
-  return p.scale < 0.f ? launch_mask<D, true, false>(p, q, k, v, o, lse) : launch_mask<D, false, false>(p, q, k, v, o, lse);
+    return p.scale < 0.f ? launch_mask<D, true, true, false>(p, q, k, v, o, lse)
+                         : launch_mask<D, false, true, false>(p, q, k, v, o, lse);
+  return p.scale < 0.f ? launch_mask<D, true, false, false>(p, q, k, v, o, lse)
+                       : launch_mask<D, false, false, false>(p, q, k, v, o, lse);
 }
 
 }  // namespace

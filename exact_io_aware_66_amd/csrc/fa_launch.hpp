@@ -15,6 +15,10 @@ struct Problem {
   const int32_t* seqlens;  // device int32[B] or nullptr
   hipStream_t stream;
   const uint8_t* block_mask = nullptr;  // device uint8[B][H][nb][nb] (nb = ceil(N/128)), or nullptr: dense
+  bool dropout = false;                 // dropout on the attention probabilities (dense attention only)
+  uint32_t drop_k0 = 0, drop_k1 = 0;    // Philox key: seed low and high words
+  uint32_t drop_off2 = 0;               // 2 offset
+  uint32_t drop_t = 256;                // keep threshold round((1 - p) 256)
 };
 
 // Workspace carve-up of the backward (byte offsets; all 256-byte aligned).
@@ -42,6 +46,8 @@ hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, co
                               const void* workspace);
 hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
                                const float* lse, float* dk, float* dv, const void* workspace);
+// Dropout keep mask as bytes (1 = kept), [B][H][N][N]: the decisions every kernel takes.
+hipError_t launch_dropout_mask(const Problem& p, uint8_t* keep);
 hipError_t launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
                              const float* lse, float* dq, const void* workspace);
 

@@ -154,6 +154,36 @@ fa_status_t fa_backward_block_sparse(const void* q, const void* k, const void* v
                                      const int32_t* seqlens, const uint8_t* block_mask, fa_dtype_t dtype,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Dropout on the attention probabilities, fused: a step of the attention chain the pages list
+ * (promptingindex page, "Why attention is memory-bound, not compute-bound": matmul, scaling,
+ * masking, softmax, dropout, matmul); the mask is regenerated in every kernel from a counter-based
+ * generator and never stored (the recomputation of NOTE-005: FlashAttention, "Method").
+ *   O = (P * Z (256 / t)) V with P the softmax of the masked, scaled scores, t = round((1 - p) 256)
+ *   (half to even, 1 <= t <= 256) and Z the keep mask: element (b, h, query i, key j) is kept when
+ *   byte e of word g of Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2,
+ *   3", SC'11) with key (seed & 0xffffffff, seed >> 32) and counter
+ *   (i, j / 32, b H + h, 2 offset + (j / 4) % 2) is below t, where j % 32 = 8 g + 4 ((j / 4) % 2) + e.
+ *   LSE is that of the undropped P.  The backward is the gradient of sum(dO * O) through the same
+ *   Z (same seed and offset).
+ *   dropout_p: 0 <= p and t >= 1 (p <= about 0.998), finite; FA_ERR_INVALID_ARGUMENT otherwise.
+ *   p = 0 reproduces fa_forward / fa_backward.  Dense attention only (no block mask).
+ * fa_dropout_mask writes Z itself as bytes (1 = kept) into keep, device uint8 [B][H][N][N],
+ * caller-owned: the decisions the two other calls take, for inspection and tests.
+ * Other arguments, layouts and errors as in fa_forward / fa_backward.
+ */
+fa_status_t fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int d, float scale, int causal,
+                               const int32_t* seqlens, float dropout_p, uint64_t seed, uint32_t offset,
+                               fa_dtype_t dtype, void* stream);
+fa_status_t fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                                const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                int B, int H, int N, int d, float scale, int causal,
+                                const int32_t* seqlens, float dropout_p, uint64_t seed, uint32_t offset,
+                                fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+fa_status_t fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset,
+                            uint8_t* keep, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

@@ -46,8 +46,9 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    """t = round((1 - p) 256); the keep probability is t / 256."""
-    t = int(round((1.0 - float(p)) * 256.0))
+    """t = round((1 - p) 256), half to even, with p taken as a float32 (the C ABI's type); the keep
+    probability is t / 256."""
+    t = int(round((1.0 - float(np.float32(p))) * 256.0))
     if not 1 <= t <= 256:
         raise ValueError("dropout probability must leave a keep threshold of 1..256 (0 <= p < 1 - 1/512)")
     return t

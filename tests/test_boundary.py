@@ -140,3 +140,35 @@ def test_block_sparse_valid_arguments_without_device_report_hip_error(lib):
     assert _fwd_bs(lib) == HIP
     assert _bwd_bs(lib) == HIP
     assert _fwd_bs(lib, N=131072) == HIP  # the largest supported sequence
+
+
+def _fwd_dr(lib, p=0.1, **kw):
+    a = dict(q=P, k=P + 4096, v=P + 8192, o=P + 12288, lse=P + 16384, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+             seqlens=None, dtype=BF16)
+    a.update(kw)
+    return lib.fa_forward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                  a["causal"], a["seqlens"], p, 1234567890123, 7, a["dtype"], None)
+
+
+@pytest.mark.parametrize("p,code", [(float("nan"), INVALID), (-0.1, INVALID), (0.999, INVALID), (1.0, INVALID),
+                                    (float("inf"), INVALID)])
+def test_dropout_probability_errors(lib, p, code):
+    assert _fwd_dr(lib, p=p) == code
+    ws = lib.fa_backward_workspace_size(2, 3, 100, 64, BF16)
+    assert lib.fa_backward_dropout(P, P + 4096, P + 8192, P + 12288, P + 24576, P + 16384, P + 20480, P + 28672,
+                                   P + 32768, 2, 3, 100, 64, 0.125, 1, None, p, 1, 0, BF16, P + 65536, ws, None) == code
+    assert lib.fa_dropout_mask(2, 3, 100, p, 1, 0, P, None) == code
+
+
+def test_dropout_other_argument_errors(lib):
+    assert _fwd_dr(lib, q=None) == INVALID
+    assert _fwd_dr(lib, d=96) == UNSUPPORTED
+    assert lib.fa_dropout_mask(2, 3, 100, 0.1, 1, 0, None, None) == INVALID
+    assert lib.fa_dropout_mask(0, 3, 100, 0.1, 1, 0, P, None) == INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_dropout_valid_arguments_without_device_report_hip_error(lib):
+    assert _fwd_dr(lib, p=0.0) == HIP
+    assert _fwd_dr(lib, p=0.998) == HIP  # round(0.002 * 256) = 1 element in 256 kept
+    assert lib.fa_dropout_mask(2, 3, 100, 0.5, 1, 0, P, None) == HIP
