@@ -240,6 +240,47 @@ def measure_block_sparse(fa, w, x, pattern: str, steps: int, dense_ms: tuple):
             "speedup_vs_dense_fwd_bwd": round((dense_ms[0] + dense_ms[1]) / (ms_f + ms_b), 3)}
 
 
+def measure_dropout(fa, w, x, p: float, steps: int, dense_ms: tuple):
+    """Forward and backward of workload w with fused dropout (fa_forward_dropout,
+    fa_backward_dropout): time per step, algorithmic FLOPs as for the dense step (every pair is
+    still computed; dropout only zeroes some in P V and dP), slowdown against the dense steps."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    sl = None if x["seqlens"] is None else x["seqlens"].to(dev)
+    o, lse = torch.empty_like(q), torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    seed = 0x5EED
+
+    def fwd(i):
+        fa.fa_forward_dropout(q, k, v, o, lse, x["scale"], w.causal, sl, p, seed, i)
+
+    def bwd(i):
+        fa.fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, x["scale"], w.causal, sl, p, seed, i, ws)
+
+    for i in range(5):
+        fwd(i)
+        bwd(i)
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for i in range(steps):
+        fwd(i)
+    e[1].record(stream)
+    for i in range(steps):
+        bwd(i)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    ms_f, ms_b = e[0].elapsed_time(e[1]) / steps, e[1].elapsed_time(e[2]) / steps
+    ff, fb = workload_flops(w, x)[:2]
+    return {"p": p, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "fwd_tflops": round(ff / (ms_f * 1e-3) / 1e12, 2),
+            "fwd_bwd_tflops": round((ff + fb) / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+            "time_vs_dense_fwd_bwd": round((ms_f + ms_b) / (dense_ms[0] + dense_ms[1]), 3)}
+
+
 def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = False):
     """Time `steps` fwd+bwd steps of workload w (inputs resident on the device): clock settling,
     warm-up, then HIP events around the timed region and around every launch."""
@@ -309,6 +350,8 @@ def main():
                     help="repeat the step untimed for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dropout", action="store_true",
+                    help="skip the fused-dropout measurement (same workload, p = 0.1)")
     ap.add_argument("--no-block-sparse", action="store_true",
                     help="skip the block-sparse measurements (same workload, two block masks)")
     ap.add_argument("--cold", action="store_true",
@@ -407,6 +450,8 @@ def main():
                      "traffic": measured_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                      "ms_per_launch": round(dom_ms, 4)},
     }
+    if not args.no_dropout:
+        out["dropout"] = measure_dropout(fa, w, x, 0.1, args.steps, (ms_fwd, ms_bwd))
     if not args.no_block_sparse:
         out["block_sparse"] = [measure_block_sparse(fa, w, x, pat, args.steps, (ms_fwd, ms_bwd))
                                for pat in ("local+global", "random")]
