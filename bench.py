@@ -281,6 +281,44 @@ def measure_dropout(fa, w, x, p: float, steps: int, dense_ms: tuple):
             "time_vs_dense_fwd_bwd": round((ms_f + ms_b) / (dense_ms[0] + dense_ms[1]), 3)}
 
 
+def kv_outer_model_bytes(B: int, H: int, N: int, d: int, bc: int, br: int) -> int:
+    """HBM bytes of the pages' K/V-outer schedule as fa_forward_kv_outer runs it: K and V (bf16) read
+    once; O (fp32), m and l initialised; then for every K/V block and every Q block, Q_i (bf16), O_i,
+    m_i and l_i read and O_i, m_i, l_i written back (the last K/V block writes O in bf16 and LSE)."""
+    tc, tr = -(-N // bc), -(-N // br)
+    del tr
+    per_head = (2 * N * d * 2                      # K, V
+                + N * d * 4 + 2 * N * 4             # initial O, m, l
+                + tc * N * (d * 2 + d * 4 + 8)      # Q_i, O_i, m_i, l_i read per K/V block
+                + (tc - 1) * N * (d * 4 + 8)        # O_i, m_i, l_i written back
+                + N * (d * 2 + 8 + 4))              # last block: O (bf16), m, l, LSE
+    return B * H * per_head
+
+
+def theorem2(fa, lds_list, N: int, d: int, BH: int):
+    """One launch of the K/V-outer schedule per LDS budget on seeded inputs; prints one JSON line each."""
+    import torch
+
+    import workloads
+    x = workloads.draw_custom(1, BH, N, d, dtype="bf16", seed=2)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = torch.empty_like(q), torch.empty(1, BH, N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_forward_kv_outer_workspace_size(1, BH, N, d), dtype=torch.uint8, device="cuda")
+    for lds in lds_list:
+        m = lds // 4
+        bc = -(-m // (4 * d))
+        br = min(bc, d)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fa.fa_forward_kv_outer(q, k, v, o, lse, x["scale"], lds, ws)
+        b.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"theorem2": True, "B": 1, "H": BH, "N": N, "d": d, "lds_bytes": lds, "M_elements": m,
+                          "Bc": bc, "Br": br, "ms": round(a.elapsed_time(b), 3),
+                          "model_bytes": kv_outer_model_bytes(1, BH, N, d, bc, br),
+                          "n2d2_over_m": N * N * d * d / m}), flush=True)
+
+
 def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = False):
     """Time `steps` fwd+bwd steps of workload w (inputs resident on the device): clock settling,
     warm-up, then HIP events around the timed region and around every launch."""
@@ -360,6 +398,10 @@ def main():
                     help="only time every workload and print one line each with its per-config roofline fraction")
     ap.add_argument("--naive-torch", action="store_true",
                     help="only time the materialising attention forward as plain torch ops (context)")
+    ap.add_argument("--theorem2", action="store_true",
+                    help="only run the pages' K/V-outer schedule (fa_forward_kv_outer) once per LDS budget "
+                         "(16, 32, 64, 128 KiB) at N=4096, d=128, 64 heads (8 per XCD, so the heads' Q and O overflow "
+                         "each XCD's 4 MB L2), for its HBM byte counters")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), to scale the HBM "
                          "byte counters of a profiler run, and exit")
@@ -386,6 +428,9 @@ def main():
     import workloads
 
     fa.load()
+    if args.theorem2:
+        theorem2(fa, [16 * 1024, 32 * 1024, 64 * 1024, 128 * 1024], 4096, 128, 64)
+        return
     if args.all_configs:
         for wid in sorted(workloads.WORKLOADS):
             w = workloads.WORKLOADS[wid]

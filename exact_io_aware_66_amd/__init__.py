@@ -11,6 +11,8 @@ missing or a call is unsupported, these functions raise.
     fa_forward_dropout(q, k, v, o, lse, scale, causal, seqlens, p, seed, offset)
     fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, p, seed, offset, workspace)
     fa_dropout_mask(B, H, N, p, seed, offset, keep)
+    fa_forward_kv_outer(q, k, v, o, lse, scale, lds_bytes, workspace)    # the pages' schedule (IO measurement)
+    fa_forward_kv_outer_workspace_size(B, H, N, d)
     fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace)
     forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
     backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
@@ -32,7 +34,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: 
           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
            "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
-           "fa_backward_dropout", "fa_dropout_mask", "fa_status_string", "fa_last_error")
+           "fa_backward_dropout", "fa_dropout_mask", "fa_forward_kv_outer", "fa_forward_kv_outer_workspace_size",
+           "fa_status_string", "fa_last_error")
 MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
 
 _lib = None
@@ -75,6 +78,10 @@ def load(path: str = LIB_PATH):
     lib.fa_backward_dropout.restype = i
     lib.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
     lib.fa_dropout_mask.restype = i
+    lib.fa_forward_kv_outer.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, sz, i, vp, sz, vp]
+    lib.fa_forward_kv_outer.restype = i
+    lib.fa_forward_kv_outer_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_forward_kv_outer_workspace_size.restype = sz
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -228,6 +235,20 @@ def fa_dropout_mask(B: int, H: int, N: int, p: float, seed: int, offset: int, ke
     if not (keep.is_cuda and keep.dtype == torch.uint8 and keep.is_contiguous() and tuple(keep.shape) == (B, H, N, N)):
         raise ValueError("keep must be a contiguous uint8 device tensor [B, H, N, N]")
     _check(lib.fa_dropout_mask(B, H, N, float(p), int(seed), int(offset), _ptr(keep), _stream(stream)))
+
+
+def fa_forward_kv_outer_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_forward_kv_outer_workspace_size(B, H, N, d))
+
+
+def fa_forward_kv_outer(q, k, v, o, lse, scale: float, lds_bytes: int, workspace, stream=None) -> None:
+    """C-ABI fa_forward_kv_outer: the pages' K/V-outer schedule with an LDS budget of lds_bytes (bf16)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, lse, workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_forward_kv_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                   int(lds_bytes), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:

@@ -337,6 +337,37 @@ fa_status_t fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed,
   return e == hipSuccess ? FA_OK : hip_fail(e, "fa_dropout_mask launch");
 }
 
+size_t fa_forward_kv_outer_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return rows * (size_t)d * 4 + 2 * rows * 4;
+}
+
+fa_status_t fa_forward_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                                int d, float scale, size_t lds_bytes, fa_dtype_t dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
+  if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the K/V-outer schedule takes bf16 inputs only");
+  if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
+      (s = check_tensor(o, "o")) != FA_OK || (s = check_f32_vec(lse, "lse")) != FA_OK)
+    return s;
+  if ((int64_t)B * H > 0x7fffffff) return fail(FA_ERR_INVALID_ARGUMENT, "B*H must be below 2^31");
+  const fa::KvOuterTiles t = fa::kv_outer_tiles(d, lds_bytes);
+  if (lds_bytes == 0 || t.Bc < 1 || t.smem > 160 * 1024)
+    return fail(FA_ERR_UNSUPPORTED, "LDS budget of %zu bytes gives tiles B_c=%d, B_r=%d needing %zu bytes (at most 160 KiB)",
+                lds_bytes, t.Bc, t.Br, t.smem);
+  const size_t need = fa_forward_kv_outer_workspace_size(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 16)) return fail(FA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  if ((s = check_device()) != FA_OK) return s;
+  const fa::Problem p = problem(B, H, N, d, scale, 0, nullptr, stream);
+  const hipError_t e = fa::launch_fwd_kv_outer(p, q, k, v, o, lse, workspace, lds_bytes);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "fa_forward_kv_outer launch");
+}
+
 fa_status_t fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
                                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                                      float scale, int causal, const int32_t* seqlens, const uint8_t* block_mask,

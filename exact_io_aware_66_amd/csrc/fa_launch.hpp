@@ -46,6 +46,15 @@ hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, co
                               const void* workspace);
 hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,
                                const float* lse, float* dk, float* dv, const void* workspace);
+// The pages' K/V-outer schedule (IO-complexity measurement): tiles from an LDS budget of lds_bytes
+// (fp32 elements), workspace = fp32 O [B][H][N][d], m and l [B][H][N].
+struct KvOuterTiles {
+  int Bc, Br;
+  size_t smem;  // LDS bytes the kernel uses for these tiles (K, V, Q, O tiles, S, two row factors)
+};
+KvOuterTiles kv_outer_tiles(int d, size_t lds_bytes);
+hipError_t launch_fwd_kv_outer(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                               void* workspace, size_t lds_bytes);
 // Dropout keep mask as bytes (1 = kept), [B][H][N][N]: the decisions every kernel takes.
 hipError_t launch_dropout_mask(const Problem& p, uint8_t* keep);
 hipError_t launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,

@@ -184,6 +184,23 @@ fa_status_t fa_backward_dropout(const void* q, const void* k, const void* v, con
 fa_status_t fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset,
                             uint8_t* keep, void* stream);
 
+/*
+ * The pages' own schedule, for measuring its HBM traffic (NOTE-005: FlashAttention, "Method" and
+ * "Key results", Theorem 2: Theta(N^2 d^2 / M) HBM accesses for d <= M <= N d).  Same O and LSE as
+ * fa_forward (no masks), computed with K/V blocks in the outer loop and Q blocks in the inner one;
+ * O, m and l are kept in HBM (in the workspace, fp32) and read and written back for every block
+ * pair.  Tiles follow the pages' rule with an LDS budget of lds_bytes held as fp32:
+ * M = lds_bytes / 4 elements, B_c = ceil(M / 4d), B_r = min(B_c, d).  One workgroup per
+ * (batch, head); fp32 vector arithmetic.  A measurement instrument, not a fast path.
+ *   dtype must be FA_DTYPE_BF16; the tiles (2 B_c d + 2 B_r d + B_r B_c + 2 B_r floats) must fit in
+ *   160 KiB of LDS and B_c >= 1, else FA_ERR_UNSUPPORTED.
+ *   workspace: at least fa_forward_kv_outer_workspace_size() bytes, 16-byte aligned, scratch.
+ */
+size_t fa_forward_kv_outer_workspace_size(int B, int H, int N, int d);
+fa_status_t fa_forward_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, int d, float scale, size_t lds_bytes, fa_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

@@ -172,3 +172,27 @@ def test_dropout_valid_arguments_without_device_report_hip_error(lib):
     assert _fwd_dr(lib, p=0.0) == HIP
     assert _fwd_dr(lib, p=0.998) == HIP  # round(0.002 * 256) = 1 element in 256 kept
     assert lib.fa_dropout_mask(2, 3, 100, 0.5, 1, 0, P, None) == HIP
+
+
+def _kvo(lib, lds=32768, ws_bytes=None, dtype=BF16, d=128, N=300):
+    ws_bytes = lib.fa_forward_kv_outer_workspace_size(2, 3, N, d) if ws_bytes is None else ws_bytes
+    return lib.fa_forward_kv_outer(P, P + 4096, P + 8192, P + 12288, P + 16384, 2, 3, N, d, 0.125, lds, dtype,
+                                   P + 65536, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(dtype=F32), UNSUPPORTED), (dict(lds=0), UNSUPPORTED),
+                                     (dict(lds=1 << 20), UNSUPPORTED), (dict(ws_bytes=16), WORKSPACE),
+                                     (dict(d=96), UNSUPPORTED)])
+def test_kv_outer_argument_errors(lib, kw, code):
+    assert _kvo(lib, **kw) == code
+
+
+def test_kv_outer_workspace_size(lib):
+    assert lib.fa_forward_kv_outer_workspace_size(2, 3, 100, 64) == 2 * 3 * 100 * (64 * 4 + 8)
+    assert lib.fa_forward_kv_outer_workspace_size(2, 3, 100, 96) == 0
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_kv_outer_valid_arguments_without_device_report_hip_error(lib):
+    assert _kvo(lib) == HIP
+    assert _kvo(lib, lds=128 * 1024) == HIP  # B_c = B_r = 64 at d = 128: 148 KiB of LDS
