@@ -13,6 +13,7 @@ missing or a call is unsupported, these functions raise.
     fa_dropout_mask(B, H, N, p, seed, offset, keep)
     fa_forward_kv_outer(q, k, v, o, lse, scale, lds_bytes, workspace)    # the pages' schedule (IO measurement)
     fa_forward_kv_outer_workspace_size(B, H, N, d)
+    fa_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, o, lse, scale, causal, seqlens)
     fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace)
     forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
     backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
@@ -35,7 +36,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: 
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
            "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
            "fa_backward_dropout", "fa_dropout_mask", "fa_forward_kv_outer", "fa_forward_kv_outer_workspace_size",
-           "fa_status_string", "fa_last_error")
+           "fa_forward_fp8", "fa_status_string", "fa_last_error")
 MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
 
 _lib = None
@@ -82,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.fa_forward_kv_outer.restype = i
     lib.fa_forward_kv_outer_workspace_size.argtypes = [i, i, i, i]
     lib.fa_forward_kv_outer_workspace_size.restype = sz
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.fa_forward_fp8.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -249,6 +252,23 @@ def fa_forward_kv_outer(q, k, v, o, lse, scale: float, lds_bytes: int, workspace
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.fa_forward_kv_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                    int(lds_bytes), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_forward_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, o, lse, scale: float,
+                   causal: bool = False, seqlens=None, stream=None) -> None:
+    """C-ABI fa_forward_fp8: q8, k8, v8 torch.float8_e4m3fn [B, H, N, 128]; o bfloat16; lse float32."""
+    lib = load()
+    B, H, N, d = _dims(q8)
+    _same(q8, k8, v8, o, lse)
+    for t in (q8, k8, v8):
+        if t.dtype != torch.float8_e4m3fn:
+            raise FAError(2, f"FP8 inputs must be torch.float8_e4m3fn (got {t.dtype})")
+    if o.dtype != torch.bfloat16:
+        raise ValueError("o must be bfloat16")
+    seqlens = _seqlens(seqlens, B, q8.device)
+    _check(lib.fa_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(descale_q), float(descale_k), float(descale_v),
+                              _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens),
+                              _stream(stream)))
 
 
 def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:

@@ -337,6 +337,30 @@ fa_status_t fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed,
   return e == hipSuccess ? FA_OK : hip_fail(e, "fa_dropout_mask launch");
 }
 
+fa_status_t fa_forward_fp8(const void* q8, const void* k8, const void* v8, float descale_q, float descale_k,
+                           float descale_v, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* seqlens, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, FA_DTYPE_BF16)) != FA_OK) return s;
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward supports d = 128 only (got %d)", d);
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return fail(FA_ERR_INVALID_ARGUMENT, "descales must be finite and positive");
+  if ((s = check_tensor(q8, "q8")) != FA_OK || (s = check_tensor(k8, "k8")) != FA_OK ||
+      (s = check_tensor(v8, "v8")) != FA_OK || (s = check_tensor(o, "o")) != FA_OK ||
+      (s = check_f32_vec(lse, "lse")) != FA_OK)
+    return s;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
+  if (fa::fwd_bf16_grid(B, H, N) > 0x7fffffff) return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
+  if ((s = check_head_bytes(N, d, FA_DTYPE_BF16)) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  p.fp8_qk_descale = descale_q * descale_k;
+  p.fp8_v_descale = descale_v;
+  const hipError_t e = fa::launch_fwd_fp8(p, q8, k8, v8, o, lse);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "fa_forward_fp8 launch");
+}
+
 size_t fa_forward_kv_outer_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;

@@ -28,6 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // 32 FP8 values: an operand of the FP8 MFMA
 
 #define FA_LDS __attribute__((address_space(3)))
 
@@ -180,6 +181,9 @@ __device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0
 // its side of the barrier; the LDS reads issued before it have all been consumed (and so have
 // completed) by then, so no lgkmcnt wait is needed for the stage that is reloaded after it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The same barrier once this wave's LDS stores have completed (lgkmcnt(0)): for tiles that the
+// waves write into LDS themselves.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Keeps the computation of x where it stands: the (empty) volatile statement consumes and
 // redefines x, so the code that produces x is not moved past later volatile statements (barriers).
 template <class T>

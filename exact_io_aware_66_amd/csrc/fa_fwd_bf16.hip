@@ -51,13 +51,18 @@ constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 128 query rows per workg
 constexpr int kFwdBc = 64;                           // keys per tile
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP>
+// F8: Q, K and V are OCP FP8 E4M3 bytes (the pointers are reinterpreted): S = K Q^T on the FP8
+// matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation, exact products), V converted exactly
+// to bf16 on its way into LDS, P V as in the bf16 path; the per-tensor descales of Q and K are folded
+// into c_log2 and that of V into o_scale.
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP, bool F8>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens,
-                                                          const uint8_t* __restrict__ bmask, Dropout dr, int nqb,
-                                                          int BH) {
+                                                          const uint8_t* __restrict__ bmask, Dropout dr, float o_scale,
+                                                          int nqb, int BH) {
+  static_assert(!F8 || (D == 128 && !SPARSE && !DROP), "the FP8 forward is built for d = 128, dense");
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = kFwdBc * D * 2;      // bytes of one K or V tile
   constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
@@ -130,14 +135,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   auto tix = [&](int t) { return SPARSE ? list_tile(tlist[t]) : t; };
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds query `query`, d = 16 ds + 8 half .. +7
-  bf16x8 qf[DS];
+  bf16x8 qf[F8 ? 1 : DS];
+  // F8: lane holds query `query`, bytes d = 64 m + 32 half .. +31 for k-step m (the same per-lane d
+  // set as the K fragment, so the product sums over every d whatever the instruction's k order)
+  constexpr int DM = D / 64;
+  i32x8 qf8[F8 ? DM : 1];
+  if constexpr (F8) {
+    const uint8_t* q8 = (const uint8_t*)Q + row0 * D;
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    if (query < N) {
-      qf[ds] = *(const bf16x8*)(Qh + (int64_t)query * D + 16 * ds + 8 * half);
-    } else {
+    for (int m = 0; m < DM; ++m) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (query < N) {
+        a = *(const u32x4*)(q8 + (int64_t)query * D + 64 * m + 32 * half);
+        b = *(const u32x4*)(q8 + (int64_t)query * D + 64 * m + 32 * half + 16);
+      }
+      qf8[m] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ds][e] = (__bf16)0.f;
+    for (int ds = 0; ds < DS; ++ds) {
+      if (query < N) {
+        qf[ds] = *(const bf16x8*)(Qh + (int64_t)query * D + 16 * ds + 8 * half);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ds][e] = (__bf16)0.f;
+      }
     }
   }
 
@@ -164,6 +186,56 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     const u32x4 rs = make_rsrc(src + (int64_t)t * kFwdBc * D, (N - t * kFwdBc) * D * 2);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kFwdWaves + wave) * 1024);
+  };
+  // F8: K tiles of 64 rows x D bytes (128-byte rows, swizzled like 64-column bf16 rows), loaded
+  // straight into LDS; V tiles loaded into registers, converted to bf16 and stored in the bf16 tile
+  // layout the P V products read.
+  constexpr int LOADS8 = kFwdBc * (D / 16) / 256;
+  uint32_t voff8[F8 ? LOADS8 : 1];
+  if constexpr (F8) {
+#pragma unroll
+    for (int n = 0; n < LOADS8; ++n) {
+      const int p = (n * kFwdWaves + wave) * 64 + lane;
+      const int r = p / (D / 16);
+      const int c = (p % (D / 16)) ^ swz<64>(r);
+      voff8[n] = (uint32_t)(r * D + 16 * c);
+    }
+  }
+  auto load_k8 = [&](int t, FA_LDS char* dst) {
+    const uint8_t* k8 = (const uint8_t*)K + (row0 + (int64_t)t * kFwdBc) * D;
+    const u32x4 rs = make_rsrc(k8, (N - t * kFwdBc) * D);
+#pragma unroll
+    for (int n = 0; n < LOADS8; ++n) bload_lds16(rs, voff8[n], dst + (n * kFwdWaves + wave) * 1024);
+  };
+  auto k8_off = [&](int row, int c) { return (uint32_t)(row * D + 16 * (c ^ swz<64>(row))); };
+  u32x4 vreg[2];  // F8: two 16-byte chunks of the next V tile per thread
+  auto load_v8 = [&](int t) {
+    const uint8_t* v8 = (const uint8_t*)V + row0 * D;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int p = n * 256 + (int)threadIdx.x;
+      const int r = min(t * kFwdBc + (p >> 3), N - 1);  // rows past N: any finite values (masked keys)
+      vreg[n] = *(const u32x4*)(v8 + (int64_t)r * D + 16 * (p & 7));
+    }
+  };
+  auto store_v8 = [&](FA_LDS char* dst) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int p = n * 256 + (int)threadIdx.x;
+      const int r = p >> 3, c8 = p & 7;
+      bf16x8 half8[2];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[n][w], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[n][w], true);
+        half8[w >> 1][4 * (w & 1) + 0] = (__bf16)lo[0];
+        half8[w >> 1][4 * (w & 1) + 1] = (__bf16)lo[1];
+        half8[w >> 1][4 * (w & 1) + 2] = (__bf16)hi[0];
+        half8[w >> 1][4 * (w & 1) + 3] = (__bf16)hi[1];
+      }
+      *(FA_LDS bf16x8*)(dst + tile_off<D>(r, 16 * c8)) = half8[0];
+      *(FA_LDS bf16x8*)(dst + tile_off<D>(r, 16 * c8 + 8)) = half8[1];
+    }
   };
 
   // S^T of two consecutive tiles: s[set][kt], lane = query column, rows = keys 32 kt + 8 (r/4) +
@@ -213,6 +285,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   // S^T(tile in kb) = K Q^T into s[set]: DS k-steps of 2 MFMAs, K fragments read two k-steps ahead;
   // `between(ds)` places VALU work after the MFMAs of k-step ds
   auto scores = [&](int set, const FA_LDS char* kb, auto&& between) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      // 2 DM FP8 MFMAs (K = 64 each); the DS VALU slots are spread two per MFMA
+      i32x8 a8[DM][2];
+#pragma unroll
+      for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int row = 32 * kt + l32;
+          const bf16x8 x = lds_read_b128(kb, k8_off(row, 4 * m + 2 * half));
+          const bf16x8 y = lds_read_b128(kb, k8_off(row, 4 * m + 2 * half + 1));
+          const u32x4 xu = __builtin_bit_cast(u32x4, x), yu = __builtin_bit_cast(u32x4, y);
+          a8[m][kt] = i32x8{(int)xu[0], (int)xu[1], (int)xu[2], (int)xu[3], (int)yu[0], (int)yu[1], (int)yu[2], (int)yu[3]};
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[set][kt] = zero16();
+#pragma unroll
+      for (int m = 0; m < DM; ++m)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          __builtin_amdgcn_sched_barrier(0);
+          s[set][kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[m][kt], qf8[m], s[set][kt], 0, 0, 0, 0, 0, 0);
+          const int slot = 2 * (2 * m + kt) * DS / (4 * DM);
+#pragma unroll
+          for (int z = 0; z < DS / (2 * DM); ++z) between(slot + z);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     bf16x8 kf[3][2];
     auto rd = [&](int ds, bf16x8 (&f)[2]) {
 #pragma unroll
@@ -305,17 +405,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
 
   // ---- prologue: K(0), K(1), V(0); S(0) and its exact update
   if (ntiles > 0) {
-    load_tile(Kh, 0, kbuf[0]);
-    if (ntiles > 1) load_tile(Kh, 1, kbuf[1]);
-    load_tile(Vh, 0, vbuf[0]);
+    if constexpr (F8) {
+      load_k8(0, kbuf[0]);
+      if (ntiles > 1) load_k8(1, kbuf[1]);
+      load_v8(0);
+      store_v8(vbuf[0]);
+    } else {
+      load_tile(Kh, 0, kbuf[0]);
+      if (ntiles > 1) load_tile(Kh, 1, kbuf[1]);
+      load_tile(Vh, 0, vbuf[0]);
+    }
   }
   wait_vmem();
-  barrier();
+  if constexpr (F8) barrier_lds();
+  else barrier();
   // The Q fragments are complete here; saying so (an unconditional use) keeps the compiler from
   // waiting for them -- and, as it cannot tell them apart, for the tile loads in flight -- inside
   // the loop.
+  if constexpr (F8) {
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) pin(qf[ds]);
+    for (int m = 0; m < DM; ++m) pin(qf8[m]);
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) pin(qf[ds]);
+  }
   if (n_wave > 0) {
     scores(0, kbuf[0], [](int) {});
     if (n_clean > 0) exact_update(0);
@@ -338,11 +451,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     constexpr int NEXT = decltype(next_tag)::value;
     const int nxt = cur ^ 1;
     wait_vmem();  // K(t+1) and V(t), issued one iteration ago, have landed
-    barrier();
-    if (t + 2 < ntiles) load_tile(Kh, t + 2, kbuf[cur]);  // over K(t), read in iteration t-1
-    if (t + 1 < ntiles) load_tile(Vh, t + 1, vbuf[nxt]);  // over V(t-1), read in iteration t-1
-    if constexpr (NEXT == kIdle) return;
-    else {
+    if constexpr (F8) barrier_lds();  // (and the bf16 V(t) written to LDS at the end of the last one)
+    else barrier();
+    if constexpr (F8) {
+      if (t + 2 < ntiles) load_k8(t + 2, kbuf[cur]);
+      if (t + 1 < ntiles) load_v8(t + 1);  // converted into vbuf[nxt] at the end of this iteration
+    } else {
+      if (t + 2 < ntiles) load_tile(Kh, t + 2, kbuf[cur]);  // over K(t), read in iteration t-1
+      if (t + 1 < ntiles) load_tile(Vh, t + 1, vbuf[nxt]);  // over V(t-1), read in iteration t-1
+    }
+    if constexpr (NEXT == kIdle) {
+      if constexpr (F8) {
+        if (t + 1 < ntiles) store_v8(vbuf[nxt]);
+      }
+      return;
+    } else {
       // phase 1: 12 P units over the DS k-steps of S(t+1) (P only when there is no next tile)
       auto ph1 = [&](int ds) {
 #pragma unroll
@@ -387,6 +510,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
         const float alpha = mask_update(nxt, t + 1);
         if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) rescale(alpha);
       }
+      if constexpr (F8) {  // V(t+1) into the other buffer (read from the next iteration on)
+        if (t + 1 < ntiles) store_v8(vbuf[nxt]);
+      }
     }
   };
 
@@ -417,9 +543,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     constexpr int NEXT = decltype(next_tag)::value;
     const float cf = t < n_clean ? c_log2 : 1.f;
     wait_vmem();
-    barrier();
-    if (t + 2 < ntiles) load_tile(Kh, t + 2, kb_cur);
-    if (t + 1 < ntiles) load_tile(Vh, t + 1, vb_nxt);
+    if constexpr (F8) barrier_lds();
+    else barrier();
+    if constexpr (F8) {
+      if (t + 2 < ntiles) load_k8(t + 2, kb_cur);
+      if (t + 1 < ntiles) load_v8(t + 1);
+    } else {
+      if (t + 2 < ntiles) load_tile(Kh, t + 2, kb_cur);
+      if (t + 1 < ntiles) load_tile(Vh, t + 1, vb_nxt);
+    }
     if constexpr (NEXT != kIdle) {
       auto ph1 = [&](int ds) {
 #pragma unroll
@@ -449,6 +581,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
         s[0][1] = s[1][1];
       }
     }
+    if constexpr (F8) {
+      if (t + 1 < ntiles) store_v8(vb_nxt);
+    }
   };
   for (; t + 1 < n_wave; ++t) run(std::integral_constant<int, kNextMasked>{}, t);
   if (t < n_wave) run(std::integral_constant<int, kNextNone>{}, t++);
@@ -458,7 +593,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   {
     const float l = add_halves(l_run);
     const bool has = l > 0.f;
-    const float inv = has ? (DROP ? dr.scale : 1.f) / l : 0.f;
+    const float inv = has ? (DROP ? dr.scale : 1.f) * (F8 ? o_scale : 1.f) / l : 0.f;
     if (query < N) {
       if (half == 0) LSE[row0 + query] = has ? (m_p + __log2f(l)) * kLn2 : -INFINITY;
       __bf16* orow = O + (row0 + query) * D;
@@ -475,15 +610,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP>
+template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP, bool F8 = false>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   const int nqb = (p.N + kFwdBr - 1) / kFwdBr;
   const int BH = p.B * p.H;
-  const float c_log2 = p.scale * kLog2e;
+  const float c_log2 = p.scale * kLog2e * (F8 ? p.fp8_qk_descale : 1.f);
   const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE, DROP>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE, DROP, F8>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2,
-                     p.seqlens, p.block_mask, dr, nqb, BH);
+                     p.seqlens, p.block_mask, dr, F8 ? p.fp8_v_descale : 1.f, nqb, BH);
   return hipGetLastError();
 }
 
@@ -512,6 +647,20 @@ hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* 
 }  // namespace
 
 int64_t fwd_bf16_grid(int B, int H, int N) { return (int64_t)((N + kFwdBr - 1) / kFwdBr) * B * H; }
+
+hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* k8, const void* v8, void* o, float* lse) {
+  const bool pad = p.seqlens != nullptr, neg = p.scale < 0.f;
+  if (p.causal) {
+    if (pad) return neg ? launch<128, true, true, true, false, false, true>(p, q8, k8, v8, o, lse)
+                        : launch<128, true, true, false, false, false, true>(p, q8, k8, v8, o, lse);
+    return neg ? launch<128, true, false, true, false, false, true>(p, q8, k8, v8, o, lse)
+               : launch<128, true, false, false, false, false, true>(p, q8, k8, v8, o, lse);
+  }
+  if (pad) return neg ? launch<128, false, true, true, false, false, true>(p, q8, k8, v8, o, lse)
+                      : launch<128, false, true, false, false, false, true>(p, q8, k8, v8, o, lse);
+  return neg ? launch<128, false, false, true, false, false, true>(p, q8, k8, v8, o, lse)
+             : launch<128, false, false, false, false, false, true>(p, q8, k8, v8, o, lse);
+}
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
   return p.d == 64 ? launch_d<64>(p, q, k, v, o, lse) : launch_d<128>(p, q, k, v, o, lse);

@@ -19,6 +19,8 @@ struct Problem {
   uint32_t drop_k0 = 0, drop_k1 = 0;    // Philox key: seed low and high words
   uint32_t drop_off2 = 0;               // 2 offset
   uint32_t drop_t = 256;                // keep threshold round((1 - p) 256)
+  float fp8_qk_descale = 1.f;           // FP8 forward: descale(Q) descale(K), folded into the score scale
+  float fp8_v_descale = 1.f;            // FP8 forward: descale(V), applied to O
 };
 
 // Workspace carve-up of the backward (byte offsets; all 256-byte aligned).
@@ -35,6 +37,8 @@ int64_t bwd_dkdv_bf16_grid(int B, int H, int N);
 int64_t bwd_dq_bf16_grid(int B, int H, int N);
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse);
+// Forward with OCP FP8 E4M3 inputs (d = 128): S on the FP8 matrix cores, P V in bf16.
+hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* k8, const void* v8, void* o, float* lse);
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse);
 // Backward stages.  prepare: D (and, for bf16, LSE log2 e) into the workspace; dkdv: dK and dV;
 // dq: dQ.  dkdv and dq read the workspace that prepare wrote and are independent of each other.

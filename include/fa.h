@@ -201,6 +201,20 @@ fa_status_t fa_forward_kv_outer(const void* q, const void* k, const void* v, voi
                                 int B, int H, int N, int d, float scale, size_t lds_bytes, fa_dtype_t dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward with FP8 inputs, the step the pages name for FlashAttention-3 (the aicassindra FlashAttention
+ * architecture page, "The architecture: every piece explained": FP8 support).  q8, k8, v8 are
+ * OCP FP8 E4M3 bytes, [B][H][N][d] (d = 128 only), with per-tensor descales: the attention is that
+ * of Q = descale_q q8, K = descale_k k8, V = descale_v v8.  S = scale Q K^T runs on the FP8 matrix
+ * cores with fp32 accumulation (every FP8 product is exact in fp32); V is converted exactly to bf16
+ * and P V runs as in the bf16 path.  o is bf16, lse fp32, masks as in fa_forward.
+ *   Errors as in fa_forward; d != 128 -> FA_ERR_UNSUPPORTED; a descale that is not finite and
+ *   positive -> FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status_t fa_forward_fp8(const void* q8, const void* k8, const void* v8, float descale_q, float descale_k,
+                           float descale_v, void* o, float* lse, int B, int H, int N, int d, float scale,
+                           int causal, const int32_t* seqlens, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

@@ -196,3 +196,18 @@ def test_kv_outer_workspace_size(lib):
 def test_kv_outer_valid_arguments_without_device_report_hip_error(lib):
     assert _kvo(lib) == HIP
     assert _kvo(lib, lds=128 * 1024) == HIP  # B_c = B_r = 64 at d = 128: 148 KiB of LDS
+
+
+def _fp8(lib, d=128, dq=0.01, dk=0.02, dv=0.03, **kw):
+    return lib.fa_forward_fp8(P, P + 4096, P + 8192, dq, dk, dv, P + 12288, P + 16384, 2, 3, 300, d, 0.09, 1, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(d=64), UNSUPPORTED), (dict(dq=0.0), INVALID), (dict(dk=-1.0), INVALID),
+                                     (dict(dv=float("nan")), INVALID), (dict(dq=float("inf")), INVALID)])
+def test_fp8_argument_errors(lib, kw, code):
+    assert _fp8(lib, **kw) == code
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_fp8_valid_arguments_without_device_report_hip_error(lib):
+    assert _fp8(lib) == HIP

@@ -131,3 +131,11 @@ def draw_block_mask(B, H, N, pattern="random", density=0.5, window=1, seed=0):
         m = m.to(torch.uint8)[None, None].expand(B, H, nb, nb).contiguous()
     return m
 
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-tensor OCP FP8 E4M3 quantisation for FP8-input tests: returns (x8, descale) with
+    x8 = float8_e4m3fn(x / descale) and descale = max|x| / 448 (448: the largest E4M3 value)."""
+    amax = float(x.abs().max())
+    descale = amax / 448.0 if amax > 0 else 1.0
+    return (x.float() / descale).to(torch.float8_e4m3fn), descale
+
