@@ -319,6 +319,39 @@ def theorem2(fa, lds_list, N: int, d: int, BH: int):
                           "n2d2_over_m": N * N * d * d / m}), flush=True)
 
 
+def measure_fp8_forward(fa, w, x, steps: int, dense_fwd_ms: float):
+    """fa_forward_fp8 on workload w with its inputs quantised to OCP FP8 E4M3 (per-tensor descales):
+    time per forward, algorithmic TFLOP/s (4 d per visible pair, as for the bf16 forward)."""
+    import torch
+
+    import workloads
+    q8, dq = workloads.quantize_fp8(x["q"])
+    k8, dk = workloads.quantize_fp8(x["k"])
+    v8, dv = workloads.quantize_fp8(x["v"])
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    sl = None if x["seqlens"] is None else x["seqlens"].cuda()
+    o = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+
+    def fwd():
+        fa.fa_forward_fp8(q8, k8, v8, dq, dk, dv, o, lse, x["scale"], w.causal, sl)
+
+    for _ in range(5):
+        fwd()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fwd()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    ff = workload_flops(w, x)[0]
+    return {"fwd_ms": round(ms, 4), "fwd_tflops": round(ff / (ms * 1e-3) / 1e12, 2),
+            "time_vs_bf16_fwd": round(ms / dense_fwd_ms, 3),
+            "note": "S on the FP8 matrix cores (half the forward's flops), P V in bf16"}
+
+
 def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = False):
     """Time `steps` fwd+bwd steps of workload w (inputs resident on the device): clock settling,
     warm-up, then HIP events around the timed region and around every launch."""
@@ -388,6 +421,8 @@ def main():
                     help="repeat the step untimed for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8-input forward measurement (same workload, inputs quantised to E4M3)")
     ap.add_argument("--no-dropout", action="store_true",
                     help="skip the fused-dropout measurement (same workload, p = 0.1)")
     ap.add_argument("--no-block-sparse", action="store_true",
@@ -495,6 +530,8 @@ def main():
                      "traffic": measured_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                      "ms_per_launch": round(dom_ms, 4)},
     }
+    if not args.no_fp8 and w.d == 128:
+        out["fp8_forward"] = measure_fp8_forward(fa, w, x, args.steps, ms_fwd)
     if not args.no_dropout:
         out["dropout"] = measure_dropout(fa, w, x, 0.1, args.steps, (ms_fwd, ms_bwd))
     if not args.no_block_sparse:
