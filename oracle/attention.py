@@ -29,7 +29,7 @@ matrix S for one (batch, head) at a time, with no tiling, no online softmax and
 no fusion.  Library primitives used as steps: ``torch.matmul``, ``torch.exp``,
 ``torch.log``, ``torch.amax``, ``torch.sum`` -- all in float64 on the CPU.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 * scale: S = scale * Q Kᵀ with the caller's float32 scale promoted to fp64;
 * mask: additive 0 / -inf.  Causal keeps key j for query i iff j <= i
   (top-left aligned, Nq = Nk = N).  Key padding keeps key j of batch b iff
