@@ -10,9 +10,11 @@
 //
 // gfx950 design (the pages' A100 tile rule B_c = ceil(M/4d), B_r = min(B_c, d) is not used; the
 // tile is set by the register file, LDS and issue model of a CDNA4 compute unit):
-//   * one workgroup = 4 waves of one (batch, head), one wave per SIMD; a wave owns 32 query rows
-//     (128 per workgroup), fits in 256 registers, and two workgroups share a compute unit so each
-//     covers the other's memory and barrier stalls;
+//   * a wave owns 32 query rows and fits in 256 registers, so two waves share each SIMD and cover
+//     each other's stalls.  Dense d = 128: one workgroup of 8 waves (256 query rows) per compute
+//     unit, so each K/V tile reaches the unit's LDS once for 256 rows.  d = 64 and block-sparse
+//     masks: workgroups of 4 waves (128 rows, the mask's block), two per compute unit (measured:
+//     the 8-wave form is 3 % faster at d = 128 and 3-7 % slower at d = 64);
 //   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16);
 //     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
 //     lane halves hold different keys of the same queries and are combined once, at the end);
@@ -45,10 +47,14 @@ static_assert(fa::kMaskBlock == FA_MASK_BLOCK && fa::kMaskBlock * fa::kMaxMaskBl
 namespace fa {
 namespace {
 
-constexpr int kFwdWaves = 4;
-constexpr int kFwdRowsPerWave = 32;                  // query rows per wave (one 32-column MFMA tile)
-constexpr int kFwdBr = kFwdWaves * kFwdRowsPerWave;  // 128 query rows per workgroup
-constexpr int kFwdBc = 64;                           // keys per tile
+constexpr int kFwdRowsPerWave = 32;  // query rows per wave (one 32-column MFMA tile)
+constexpr int kFwdBc = 64;           // keys per tile
+// Waves per workgroup (the workgroup's query block is 32 rows per wave).
+template <int D, bool SPARSE>
+constexpr int fwd_waves() { return (D == 128 && !SPARSE) ? 8 : 4; }
+constexpr int kFwdMaxBr = 8 * kFwdRowsPerWave;  // largest query block
+constexpr int kFwdMinBr = 4 * kFwdRowsPerWave;  // smallest query block (the block-sparse one)
+static_assert(kFwdMinBr == fa::kMaskBlock, "a block-sparse query block is one row of mask blocks");
 constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before the maximum is raised
 
 // F8: Q, K and V are OCP FP8 E4M3 bytes (the pointers are reinterpreted): S = K Q^T on the FP8
@@ -56,16 +62,19 @@ constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before t
 // to bf16 on its way into LDS, P V as in the bf16 path; the per-tensor descales of Q and K are folded
 // into c_log2 and that of V into o_scale.
 template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP, bool F8>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SPARSE>())) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens,
                                                           const uint8_t* __restrict__ bmask, Dropout dr, float o_scale,
                                                           int nqb, int BH) {
   static_assert(!F8 || (D == 128 && !SPARSE && !DROP), "the FP8 forward is built for d = 128, dense");
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int TILE = kFwdBc * D * 2;      // bytes of one K or V tile
-  constexpr int LOADS = kFwdBc * CH / 256;  // 16-byte loads per thread per tile
+  constexpr int WAVES = fwd_waves<D, SPARSE>();
+  constexpr int NT = 64 * WAVES;           // threads per workgroup
+  constexpr int BR = WAVES * kFwdRowsPerWave;  // query rows per workgroup
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int TILE = kFwdBc * D * 2;     // bytes of one K or V tile
+  constexpr int LOADS = kFwdBc * CH / NT;  // 16-byte loads per thread per tile
   constexpr int DS = D / 16;                // k-steps of S = K Q^T
   constexpr int DT = D / 32;                // 32-wide d tiles of O^T
   // Separate LDS arrays, each referenced statically, so that the compiler sees which buffer every
@@ -105,10 +114,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   const __bf16* Vh = V + row0 * D;
 
   const int L = PADDED ? clamp_len(seqlens, b, N) : N;  // keys >= L are invisible
-  const int q0 = qblock * kFwdBr;
+  const int q0 = qblock * BR;
   const int qw = q0 + wave * kFwdRowsPerWave;
   const int query = qw + l32;
-  const int kv_end = CAUSAL ? min(L, q0 + kFwdBr) : L;
+  const int kv_end = CAUSAL ? min(L, q0 + BR) : L;
   int ntiles = (kv_end + kFwdBc - 1) / kFwdBc;  // tiles the workgroup loads
   const int wave_end = CAUSAL ? min(L, qw + kFwdRowsPerWave) : L;
   int n_wave = (wave_end + kFwdBc - 1) / kFwdBc;  // tiles this wave computes (>= 1 when L > 0)
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
   uint32_t voff[LOADS];
 #pragma unroll
   for (int n = 0; n < LOADS; ++n) {
-    const int p = (n * kFwdWaves + wave) * 64 + lane;
+    const int p = (n * WAVES + wave) * 64 + lane;
     const int r = p / CH;
     const int c = (p % CH) ^ swz<D>(r);
     voff[n] = (uint32_t)(r * D + 8 * c) * 2;
@@ -185,17 +194,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     t = tix(t);
     const u32x4 rs = make_rsrc(src + (int64_t)t * kFwdBc * D, (N - t * kFwdBc) * D * 2);
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kFwdWaves + wave) * 1024);
+    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * WAVES + wave) * 1024);
   };
   // F8: K tiles of 64 rows x D bytes (128-byte rows, swizzled like 64-column bf16 rows), loaded
   // straight into LDS; V tiles loaded into registers, converted to bf16 and stored in the bf16 tile
   // layout the P V products read.
-  constexpr int LOADS8 = kFwdBc * (D / 16) / 256;
+  constexpr int LOADS8 = kFwdBc * (D / 16) / NT;
   uint32_t voff8[F8 ? LOADS8 : 1];
   if constexpr (F8) {
 #pragma unroll
     for (int n = 0; n < LOADS8; ++n) {
-      const int p = (n * kFwdWaves + wave) * 64 + lane;
+      const int p = (n * WAVES + wave) * 64 + lane;
       const int r = p / (D / 16);
       const int c = (p % (D / 16)) ^ swz<64>(r);
       voff8[n] = (uint32_t)(r * D + 16 * c);
@@ -205,23 +214,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
     const uint8_t* k8 = (const uint8_t*)K + (row0 + (int64_t)t * kFwdBc) * D;
     const u32x4 rs = make_rsrc(k8, (N - t * kFwdBc) * D);
 #pragma unroll
-    for (int n = 0; n < LOADS8; ++n) bload_lds16(rs, voff8[n], dst + (n * kFwdWaves + wave) * 1024);
+    for (int n = 0; n < LOADS8; ++n) bload_lds16(rs, voff8[n], dst + (n * WAVES + wave) * 1024);
   };
   auto k8_off = [&](int row, int c) { return (uint32_t)(row * D + 16 * (c ^ swz<64>(row))); };
-  u32x4 vreg[2];  // F8: two 16-byte chunks of the next V tile per thread
+  u32x4 vreg[2];  // F8: this thread's 16-byte chunks of the next V tile (512 / NT of them)
   auto load_v8 = [&](int t) {
     const uint8_t* v8 = (const uint8_t*)V + row0 * D;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int p = n * 256 + (int)threadIdx.x;
+    for (int n = 0; n < 512 / NT; ++n) {
+      const int p = n * NT + (int)threadIdx.x;
       const int r = min(t * kFwdBc + (p >> 3), N - 1);  // rows past N: any finite values (masked keys)
       vreg[n] = *(const u32x4*)(v8 + (int64_t)r * D + 16 * (p & 7));
     }
   };
   auto store_v8 = [&](FA_LDS char* dst) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int p = n * 256 + (int)threadIdx.x;
+    for (int n = 0; n < 512 / NT; ++n) {
+      const int p = n * NT + (int)threadIdx.x;
       const int r = p >> 3, c8 = p & 7;
       bf16x8 half8[2];
 #pragma unroll
@@ -612,11 +621,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restri
 
 template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP, bool F8 = false>
 hipError_t launch(const Problem& p, const void* q, const void* k, const void* v, void* o, float* lse) {
-  const int nqb = (p.N + kFwdBr - 1) / kFwdBr;
+  constexpr int WAVES = fwd_waves<D, SPARSE>();
+  constexpr int BR = WAVES * kFwdRowsPerWave;
+  const int nqb = (p.N + BR - 1) / BR;
   const int BH = p.B * p.H;
   const float c_log2 = p.scale * kLog2e * (F8 ? p.fp8_qk_descale : 1.f);
   const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE, DROP, F8>), dim3((unsigned)(nqb * BH)), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED, NEG, SPARSE, DROP, F8>), dim3((unsigned)(nqb * BH)), dim3(64 * WAVES), 0, p.stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p.H, p.N, c_log2,
                      p.seqlens, p.block_mask, dr, F8 ? p.fp8_v_descale : 1.f, nqb, BH);
   return hipGetLastError();
@@ -646,7 +657,8 @@ hipError_t launch_d(const Problem& p, const void* q, const void* k, const void* 
 
 }  // namespace
 
-int64_t fwd_bf16_grid(int B, int H, int N) { return (int64_t)((N + kFwdBr - 1) / kFwdBr) * B * H; }
+// The largest grid any forward instantiation launches (the 128-row query blocks).
+int64_t fwd_bf16_grid(int B, int H, int N) { return (int64_t)((N + kFwdMinBr - 1) / kFwdMinBr) * B * H; }
 
 hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* k8, const void* v8, void* o, float* lse) {
   const bool pad = p.seqlens != nullptr, neg = p.scale < 0.f;
