@@ -118,10 +118,11 @@ def test_empty_and_clamped_lengths(fa, d):
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.3])
-def test_unusual_scales(fa, scale):
-    x = workloads.draw_custom(1, 2, 200, 64, dtype="bf16", causal=True, seed=5)
+@pytest.mark.parametrize("d", [64, 128])
+def test_unusual_scales(fa, scale, d):
+    x = workloads.draw_custom(1, 2, 300, d, dtype="bf16", causal=True, seed=5)
     x["scale"] = scale
-    _say(f"[parity] scale={scale}")
+    _say(f"[parity] scale={scale} d={d} N=300")
     got = run_gpu(fa, x)
     report = []
     fails = _compare_full(x, got, report)
