@@ -419,11 +419,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 
   // ---- dK = scale dS^T Q, dV: lane holds key my_key, d = 32 dt + 8 gq + 4 half + 0..3.  Keys at
   // or past the valid length are hidden from every query: their gradients are zero (selected, not
-  // multiplied: their unmasked accumulators may hold any value).
-  if (my_key < N) {
-    const bool live = !PADDED || my_key < L;
-    __bf16* dkrow = dK + (row0 + my_key) * D;
-    __bf16* dvrow = dV + (row0 + my_key) * D;
+  // multiplied: their unmasked accumulators may hold any value).  A store of the accumulator layout
+  // would write 8-byte pieces of 32 rows per instruction; instead each wave stages its 32 rows of dK
+  // and dV in its own LDS stage (256-byte rows, the tile swizzle) and writes them back as whole
+  // 16-byte chunks, 64 / CH full rows per instruction.
+  static_assert(2 * kBwdKeysPerWave * D * 2 <= STAGE, "a wave's dK and dV rows fit in one LDS stage");
+  barrier();  // every wave is done with the stages of the query tiles
+  {
+    FA_LDS char* const ep = wave == 0 ? (FA_LDS char*)st0_raw
+                            : wave == 1 ? (FA_LDS char*)st1_raw
+                            : wave == 2 ? (FA_LDS char*)st2_raw : (FA_LDS char*)st3_raw;
+    constexpr int VB = kBwdKeysPerWave * D * 2;  // bytes of the wave's dK rows (dV rows follow)
+    const bool live = (!PADDED || my_key < L) && my_key < N;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -435,9 +442,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
           kx[e] = live ? dkt[dt][4 * gq + e] * scale : 0.f;
           vx[e] = live ? dvt[dt][4 * gq + e] * (DROP ? dr.scale : 1.f) : 0.f;
         }
-        *(bf16x4*)(dkrow + d0) = pack4(kx[0], kx[1], kx[2], kx[3]);
-        *(bf16x4*)(dvrow + d0) = pack4(vx[0], vx[1], vx[2], vx[3]);
+        *(FA_LDS bf16x4*)(ep + tile_off<D>(l32, d0)) = pack4(kx[0], kx[1], kx[2], kx[3]);
+        *(FA_LDS bf16x4*)(ep + VB + tile_off<D>(l32, d0)) = pack4(vx[0], vx[1], vx[2], vx[3]);
       }
+    constexpr int CHUNKS = kBwdKeysPerWave * CH / 64;  // 16-byte chunks per lane and tensor
+#pragma unroll
+    for (int n = 0; n < CHUNKS; ++n) {
+      const int pch = n * 64 + lane;
+      const int r = pch / CH, c = pch % CH;
+      const int key = kw + r;
+      const bf16x8 kv = lds_read_b128(ep, tile_off<D>(r, 8 * c));
+      const bf16x8 vv = lds_read_b128(ep + VB, tile_off<D>(r, 8 * c));
+      if (key < N) {
+        *(bf16x8*)(dK + (row0 + key) * D + 8 * c) = kv;
+        *(bf16x8*)(dV + (row0 + key) * D + 8 * c) = vv;
+      }
+    }
   }
 }
 

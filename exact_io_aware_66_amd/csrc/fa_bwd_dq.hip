@@ -290,17 +290,33 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   if (t < ntiles) step(S0{}, t);
   if (NS > 2 && t + 1 < ntiles) step(S1{}, t + 1);
 
-  // ---- epilogue: dQ = scale acc (bf16, RNE); lane holds query `query`, d = 32 dt + 8 gq + 4 half + 0..3
-  if (query < N) {
-    __bf16* drow = dQ + (row0 + query) * D;
+  // ---- epilogue: dQ = scale acc (bf16, RNE); lane holds query `query`, d = 32 dt + 8 gq + 4 half + 0..3.
+  // A store of this layout would write 8-byte pieces of 32 rows per instruction; instead each wave
+  // stages its 32 rows in half of a K/V stage (256-byte rows, the tile swizzle) and writes them back as
+  // whole 16-byte chunks, 64 / CH full rows per instruction.
+  constexpr int RB = kDqRowsPerWave * D * 2;  // bytes of a wave's dQ rows
+  static_assert(2 * RB <= TILE && kDqWaves <= 8, "two waves' rows fit in one K or V stage");
+  barrier();  // every wave is done with the K/V stages
+  {
+    const int pair = wave >> 1;
+    FA_LDS char* const ep = (pair == 0 ? kst[0] : pair == 1 ? kst[1] : pair == 2 ? vst[0] : vst[1]) + (wave & 1) * RB;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = 32 * dt + 8 * gq + 4 * half;
-        *(bf16x4*)(drow + d0) = pack4(acc[dt][4 * gq] * scale, acc[dt][4 * gq + 1] * scale,
-                                      acc[dt][4 * gq + 2] * scale, acc[dt][4 * gq + 3] * scale);
+        *(FA_LDS bf16x4*)(ep + tile_off<D>(l32, d0)) =
+            pack4(acc[dt][4 * gq] * scale, acc[dt][4 * gq + 1] * scale, acc[dt][4 * gq + 2] * scale,
+                  acc[dt][4 * gq + 3] * scale);
       }
+    constexpr int CHUNKS = kDqRowsPerWave * CH / 64;  // 16-byte chunks per lane
+#pragma unroll
+    for (int n = 0; n < CHUNKS; ++n) {
+      const int pch = n * 64 + lane;
+      const int r = pch / CH, c = pch % CH;
+      const bf16x8 x = lds_read_b128(ep, tile_off<D>(r, 8 * c));
+      if (qw + r < N) *(bf16x8*)(dQ + (row0 + qw + r) * D + 8 * c) = x;
+    }
   }
 }
 

@@ -598,23 +598,35 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
   if (t < n_wave) run(std::integral_constant<int, kNextNone>{}, t++);
   for (; t < ntiles; ++t) run(std::integral_constant<int, kIdle>{}, t);
 
-  // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.  A store of the accumulator layout
+  // would write 8-byte pieces of 32 rows per instruction; instead each wave stages its 32 rows of O in
+  // half of a K or V buffer (256-byte rows, the tile swizzle) and writes them back as whole 16-byte
+  // chunks, 64 / CH full rows per instruction.
+  constexpr int RB = kFwdRowsPerWave * D * 2;  // bytes of a wave's O rows
+  static_assert(2 * RB <= TILE && WAVES <= 8, "two waves' rows fit in one K or V buffer");
+  barrier();  // every wave is done with the K/V buffers
   {
     const float l = add_halves(l_run);
     const bool has = l > 0.f;
     const float inv = has ? (DROP ? dr.scale : 1.f) * (F8 ? o_scale : 1.f) / l : 0.f;
-    if (query < N) {
-      if (half == 0) LSE[row0 + query] = has ? (m_p + __log2f(l)) * kLn2 : -INFINITY;
-      __bf16* orow = O + (row0 + query) * D;
+    if (query < N && half == 0) LSE[row0 + query] = has ? (m_p + __log2f(l)) * kLn2 : -INFINITY;
+    const int pair = wave >> 1;
+    FA_LDS char* const ep = (pair == 0 ? kbuf[0] : pair == 1 ? kbuf[1] : pair == 2 ? vbuf[0] : vbuf[1]) + (wave & 1) * RB;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int d0 = 32 * dt + 8 * gq + 4 * half;
-          const bf16x4 v4 = pack4(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv, acc[dt][4 * gq + 2] * inv,
-                                  acc[dt][4 * gq + 3] * inv);
-          *(bf16x4*)(orow + d0) = v4;
-        }
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dt + 8 * gq + 4 * half;
+        *(FA_LDS bf16x4*)(ep + tile_off<D>(l32, d0)) =
+            pack4(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv, acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
+      }
+    constexpr int CHUNKS = kFwdRowsPerWave * CH / 64;  // 16-byte chunks per lane
+#pragma unroll
+    for (int n = 0; n < CHUNKS; ++n) {
+      const int pch = n * 64 + lane;
+      const int r = pch / CH, c = pch % CH;
+      const bf16x8 x = lds_read_b128(ep, tile_off<D>(r, 8 * c));
+      if (qw + r < N) *(bf16x8*)(O + (row0 + qw + r) * D + 8 * c) = x;
     }
   }
 }
