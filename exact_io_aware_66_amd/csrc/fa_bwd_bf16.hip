@@ -193,18 +193,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
     }
     // Wave w fetches 64 rows of statistic w & 1 (0: LSE log2 e, 1: D) into its own 256-byte slot.
     const float* stat = (wave & 1) ? DELTA + row0 : LSE2 + row0;
+    // One buffer resource per tensor over the whole head (built once): a tile's byte offset goes into
+    // the per-lane offset, which the range check covers, so rows past N still read as zeros.
+    const u32x4 rq = make_rsrc(Qh, N * D * 2);
+    const u32x4 rg = make_rsrc(dOh, N * D * 2);
+    const u32x4 rs = make_rsrc(stat, N * 4);
     auto load_tile = [&](int u, FA_LDS char* dst) {
       const int qbase = (SPARSE ? list_tile(tlist[u]) : it0 + u) * BR;
-      const int left = N - qbase;  // rows of the head from qbase on (>= 1)
-      const u32x4 rq = make_rsrc(Qh + (int64_t)qbase * D, left * D * 2);
-      const u32x4 rg = make_rsrc(dOh + (int64_t)qbase * D, left * D * 2);
+      const uint32_t tb = (uint32_t)qbase * D * 2;
 #pragma unroll
       for (int n = 0; n < LOADS; ++n) {
         const int slot = (n * kBwdWaves + wave) * 64;
-        bload_lds16(rq, voff[n], dst + slot * 16);
-        bload_lds16(rg, voff[n], dst + QTILE + slot * 16);
+        const uint32_t off = voff[n] + tb;
+        bload_lds16(rq, off, dst + slot * 16);
+        bload_lds16(rg, off, dst + QTILE + slot * 16);
       }
-      bload_lds4(make_rsrc(stat + qbase, left * 4), lane * 4, dst + 2 * QTILE + wave * 256);
+      bload_lds4(rs, (uint32_t)(qbase + lane) * 4, dst + 2 * QTILE + wave * 256);
     };
 
     // S and dP of two consecutive tiles (set u % 2 holds tile u): lane = key my_key, rows = queries

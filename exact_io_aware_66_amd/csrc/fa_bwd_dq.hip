@@ -157,11 +157,13 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     const int c = (p % CH) ^ swz<D>(r);
     voff[n] = (uint32_t)(r * D + 8 * c) * 2;
   }
-  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
-    t = tix(t);
-    const u32x4 rs = make_rsrc(src + (int64_t)t * kDqBc * D, (N - t * kDqBc) * D * 2);
+  // One buffer resource per tensor over the whole head (built once): a tile's byte offset goes into the
+  // per-lane offset, which the range check covers, so rows past N still read as zeros.
+  const u32x4 rK = make_rsrc(Kh, N * D * 2), rV = make_rsrc(Vh, N * D * 2);
+  auto load_tile = [&](const u32x4& rs, int t, FA_LDS char* dst) {
+    const uint32_t tb = (uint32_t)tix(t) * kDqBc * D * 2;
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * kDqWaves + wave) * 1024);
+    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n] + tb, dst + (n * kDqWaves + wave) * 1024);
   };
 
   const int g = lane >> 4, j = lane & 15;
@@ -257,16 +259,16 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     else wait_vmem();
     barrier();
     if (t + NS - 1 < ntiles) {
-      load_tile(Kh, t + NS - 1, kst[(S + NS - 1) % NS]);
-      load_tile(Vh, t + NS - 1, vst[(S + NS - 1) % NS]);
+      load_tile(rK, t + NS - 1, kst[(S + NS - 1) % NS]);
+      load_tile(rV, t + NS - 1, vst[(S + NS - 1) % NS]);
     }
     if (t < n_wave && mine(t)) tile(tix(t), kst[S], vst[S]);
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
     if (i < ntiles) {
-      load_tile(Kh, i, kst[i]);
-      load_tile(Vh, i, vst[i]);
+      load_tile(rK, i, kst[i]);
+      load_tile(rV, i, vst[i]);
     }
   // The stationary operands are complete here; saying so (an unconditional use) keeps the compiler
   // from waiting for them -- and, as it cannot tell them apart, for the tile loads in flight --

@@ -190,11 +190,13 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
     const int c = (p % CH) ^ swz<D>(r);
     voff[n] = (uint32_t)(r * D + 8 * c) * 2;
   }
-  auto load_tile = [&](const __bf16* src, int t, FA_LDS char* dst) {
-    t = tix(t);
-    const u32x4 rs = make_rsrc(src + (int64_t)t * kFwdBc * D, (N - t * kFwdBc) * D * 2);
+  // One buffer resource per tensor over the whole head (built once): a tile's byte offset goes into the
+  // per-lane offset, which the range check covers, so rows past N still read as zeros.
+  const u32x4 rK = make_rsrc(Kh, N * D * 2), rV = make_rsrc(Vh, N * D * 2);
+  auto load_tile = [&](const u32x4& rs, int t, FA_LDS char* dst) {
+    const uint32_t tb = (uint32_t)tix(t) * kFwdBc * D * 2;
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n], dst + (n * WAVES + wave) * 1024);
+    for (int n = 0; n < LOADS; ++n) bload_lds16(rs, voff[n] + tb, dst + (n * WAVES + wave) * 1024);
   };
   // F8: K tiles of 64 rows x D bytes (128-byte rows, swizzled like 64-column bf16 rows), loaded
   // straight into LDS; V tiles loaded into registers, converted to bf16 and stored in the bf16 tile
@@ -420,9 +422,9 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
       load_v8(0);
       store_v8(vbuf[0]);
     } else {
-      load_tile(Kh, 0, kbuf[0]);
-      if (ntiles > 1) load_tile(Kh, 1, kbuf[1]);
-      load_tile(Vh, 0, vbuf[0]);
+      load_tile(rK, 0, kbuf[0]);
+      if (ntiles > 1) load_tile(rK, 1, kbuf[1]);
+      load_tile(rV, 0, vbuf[0]);
     }
   }
   wait_vmem();
@@ -466,8 +468,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
       if (t + 2 < ntiles) load_k8(t + 2, kbuf[cur]);
       if (t + 1 < ntiles) load_v8(t + 1);  // converted into vbuf[nxt] at the end of this iteration
     } else {
-      if (t + 2 < ntiles) load_tile(Kh, t + 2, kbuf[cur]);  // over K(t), read in iteration t-1
-      if (t + 1 < ntiles) load_tile(Vh, t + 1, vbuf[nxt]);  // over V(t-1), read in iteration t-1
+      if (t + 2 < ntiles) load_tile(rK, t + 2, kbuf[cur]);  // over K(t), read in iteration t-1
+      if (t + 1 < ntiles) load_tile(rV, t + 1, vbuf[nxt]);  // over V(t-1), read in iteration t-1
     }
     if constexpr (NEXT == kIdle) {
       if constexpr (F8) {
@@ -558,8 +560,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
       if (t + 2 < ntiles) load_k8(t + 2, kb_cur);
       if (t + 1 < ntiles) load_v8(t + 1);
     } else {
-      if (t + 2 < ntiles) load_tile(Kh, t + 2, kb_cur);
-      if (t + 1 < ntiles) load_tile(Vh, t + 1, vb_nxt);
+      if (t + 2 < ntiles) load_tile(rK, t + 2, kb_cur);
+      if (t + 1 < ntiles) load_tile(rV, t + 1, vb_nxt);
     }
     if constexpr (NEXT != kIdle) {
       auto ph1 = [&](int ds) {
