@@ -5,16 +5,18 @@
     python bench.py --all-configs      (every workload, its fraction of the per-config roofline)
     python bench.py --naive-torch      (the materialising attention as plain torch ops; context)
 
-One step = one forward (fa_forward) plus one backward (fa_backward_prepare, fa_backward_dkdv,
-fa_backward_dq -- exactly what fa_backward runs) over one batch of the synthetic workload,
-inputs resident in HBM.  Under sustained load the GPU's power management needs about a third of a
+One step = one forward (fa_forward) plus one backward (fa_backward_dq_prepare, then fa_backward_dkdv:
+exactly what fa_backward runs for dense bf16) over one batch of the synthetic workload,
+inputs resident in HBM.  The whole-job time (`value`, `ms_per_step`) comes from K steps with no event
+between the kernels; a second run of K steps with an event around every launch gives each kernel's
+average duration (an event recorded between two kernels costs the stream a few microseconds).  Under
+sustained load the GPU's power management needs about a third of a
 second to reach its steady state: the clocks ramp up over the first tens of milliseconds, and about
 0.27 s in, a one-time throttle stalls the queue for ~60 ms and runs the next ~50 ms at reduced
 clocks (measured per 10-step batch over 2 s of this step; no further event followed).  So the step
 is first repeated untimed for --settle-ms (default 1000 ms, well past that transient); then W
-untimed steps, then K timed steps bracketed by synchronisation and HIP events on the stream the
-kernels run on; per-stage HIP events inside the timed region give the average duration of each
-kernel launch.
+untimed steps, then the two timed runs of K steps, each bracketed by synchronisation and HIP events
+on the stream the kernels run on.
 
 FLOPs are algorithmic: forward 4 d per visible (query, key) pair (QK^T and PV), backward 2.5x
 forward (QK^T recomputed, dO V^T, P^T dO, dS^T Q, dS K), of which the dK/dV pass is credited with
@@ -381,18 +383,16 @@ def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = Fa
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(e=None):
         if e: e[0].record(stream)
         fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
         if e: e[1].record(stream)
-        fa.fa_backward_prepare(o, do, lse, ws)
+        fa.fa_backward_dq_prepare(q, k, v, o, do, lse, dq, scale, causal, sl, ws)
         if e: e[2].record(stream)
         fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale, causal, sl, ws)
         if e: e[3].record(stream)
-        fa.fa_backward_dq(q, k, v, do, lse, dq, scale, causal, sl, ws)
-        if e: e[4].record(stream)
 
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
@@ -402,24 +402,40 @@ def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = Fa
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # The whole-job time: K steps with nothing but the kernels between two events (an event recorded
+    # between kernels costs the stream a few microseconds of its own, so the per-kernel events are
+    # kept out of this loop).  Then K more steps with an event around every launch, for the
+    # per-kernel durations.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
+    if scratch is None:
+        t_start.record(stream)
+        for i in range(steps):
+            step()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = t_start.elapsed_time(t_end) / steps
+    i_start = torch.cuda.Event(enable_timing=True)
+    i_end = torch.cuda.Event(enable_timing=True)
+    i_start.record(stream)
     for i in range(steps):
         if scratch is not None:
             scratch.fill_(i & 0xFF)
         step(ev[i])
-    t_end.record(stream)
+    i_end.record(stream)
     torch.cuda.synchronize()
-    names = ("fwd", "pre", "dkdv", "dq")
+    if scratch is not None:  # cold steps: the scratch writes are outside the kernels, not the job
+        ms_step = None
+    names = ("fwd", "dq", "dkdv")
     per = {n: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, n in enumerate(names)}
-    r = {"ms_step": t_start.elapsed_time(t_end) / steps, "flops_fwd": flops_fwd, "flops_bwd": flops_bwd,
+    r = {"ms_step": ms_step, "ms_step_instrumented": i_start.elapsed_time(i_end) / steps,
+         "flops_fwd": flops_fwd, "flops_bwd": flops_bwd,
          "flops_dkdv": flops_dkdv, "flops_dq": flops_dq,
          "med": {n: round(statistics.median(v), 4) for n, v in per.items()},
          "min": {n: round(min(v), 4) for n, v in per.items()}}
     for n in names:
         r["ms_" + n] = sum(per[n]) / steps
-    r["ms_bwd"] = r["ms_pre"] + r["ms_dkdv"] + r["ms_dq"]
+    r["ms_bwd"] = r["ms_dq"] + r["ms_dkdv"]
     return r
 
 
@@ -513,7 +529,7 @@ def main():
               flush=True)
         return
     r = measure(fa, w, x, args.steps, args.warmup, args.settle_ms)
-    ms_step, ms_fwd, ms_pre, ms_dkdv, ms_dq = r["ms_step"], r["ms_fwd"], r["ms_pre"], r["ms_dkdv"], r["ms_dq"]
+    ms_step, ms_fwd, ms_dkdv, ms_dq = r["ms_step"], r["ms_fwd"], r["ms_dkdv"], r["ms_dq"]
     ms_bwd = r["ms_bwd"]
     flops_fwd, flops_bwd, flops_dkdv, flops_dq = r["flops_fwd"], r["flops_bwd"], r["flops_dkdv"], r["flops_dq"]
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
@@ -524,7 +540,9 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_with_kernel_events": round(r["ms_step_instrumented"], 4), "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "key_padding": w.padded, "q_std": w.q_std, "parallelism": "single GPU"},
@@ -532,9 +550,10 @@ def main():
         "fwd": {"ms": round(ms_fwd, 4), "ms_median": r["med"]["fwd"], "ms_min": r["min"]["fwd"],
                 "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
                 "pct_of_mfma_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
-        "bwd": {"ms": round(ms_bwd, 4), "ms_prepare": round(ms_pre, 4), "ms_dkdv": round(ms_dkdv, 4),
-                "ms_dq": round(ms_dq, 4), "ms_median": {k: r["med"][k] for k in ("pre", "dkdv", "dq")},
-                "ms_min": {k: r["min"][k] for k in ("pre", "dkdv", "dq")},
+        "bwd": {"ms": round(ms_bwd, 4), "ms_dq": round(ms_dq, 4), "ms_dkdv": round(ms_dkdv, 4),
+                "dq_includes_prepare": True,
+                "ms_median": {k: r["med"][k] for k in ("dq", "dkdv")},
+                "ms_min": {k: r["min"][k] for k in ("dq", "dkdv")},
                 "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2)},
         "flops": {"fwd": flops_fwd, "bwd": flops_bwd},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

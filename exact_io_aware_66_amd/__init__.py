@@ -34,7 +34,7 @@ FA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_MISALIGNED",
           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
-           "fa_backward_dq", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
+           "fa_backward_dq", "fa_backward_dq_prepare", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
            "fa_backward_dropout", "fa_dropout_mask", "fa_forward_kv_outer", "fa_forward_kv_outer_workspace_size",
            "fa_forward_fp8", "fa_status_string", "fa_last_error")
 MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH):
     lib.fa_backward_dkdv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
     lib.fa_backward_dq.restype = i
+    lib.fa_backward_dq_prepare.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_backward_dq_prepare.restype = i
     lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, vp]
     lib.fa_forward_block_sparse.restype = i
     lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
@@ -291,6 +293,19 @@ def fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale: float, causal: bool = Fals
     _check(lib.fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
                                 B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                                 _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_backward_dq_prepare(q, k, v, o, do, lse, dq, scale: float, causal: bool = False, seqlens=None,
+                           workspace=None, stream=None) -> None:
+    """fa_backward_prepare and fa_backward_dq in one call: writes dq and the workspace's row statistics."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, do, lse, dq, workspace)
+    seqlens = _seqlens(seqlens, B, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_backward_dq_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                      B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
+                                      _ptr(workspace), nbytes, _stream(stream)))
 
 
 def fa_backward_dq(q, k, v, do, lse, dq, scale: float, causal: bool = False, seqlens=None, workspace=None,

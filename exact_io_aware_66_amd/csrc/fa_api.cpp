@@ -158,6 +158,15 @@ fa_status_t run_dq(const fa::Problem& p, fa_dtype_t dtype, const void* q, const 
   return e == hipSuccess ? FA_OK : hip_fail(e, "backward dQ launch");
 }
 
+// The dQ pass with the prepare stage folded in (bf16): also writes D and LSE log2(e) into the workspace.
+fa_status_t run_dq_prepare(fa::Problem p, const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* workspace) {
+  p.pre_o = o;
+  p.pre_lse = lse;
+  hipError_t e = fa::launch_bwd_dq_bf16(p, q, k, v, dO, dq, workspace);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "backward dQ (with prepare) launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +265,11 @@ fa_status_t backward_impl(const void* q, const void* k, const void* v, const voi
   fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   p.block_mask = block_mask;
   set_dropout(p, drop, t);
+  if (dtype == FA_DTYPE_BF16 && !drop.on && block_mask == nullptr) {
+    // dense bf16: the dQ pass forms the row statistics itself, then the dK/dV pass reads them
+    if ((s = run_dq_prepare(p, q, k, v, o, dO, lse, dq, workspace)) != FA_OK) return s;
+    return run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace);
+  }
   if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
   if ((s = run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace)) != FA_OK) return s;
   return run_dq(p, dtype, q, k, v, dO, lse, dq, workspace);
@@ -422,6 +436,23 @@ fa_status_t fa_backward_dkdv(const void* q, const void* k, const void* v, const 
     return s;
   if ((s = check_device()) != FA_OK) return s;
   return run_dkdv(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dk, dv, workspace);
+}
+
+fa_status_t fa_backward_dq_prepare(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                   const float* lse, void* dq, int B, int H, int N, int d, float scale, int causal,
+                                   const int32_t* seqlens, fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = validate_stage(q, k, v, dO, lse, {{dq, "dq"}}, B, H, N, d, scale, seqlens, dtype, workspace,
+                          workspace_bytes)) != FA_OK)
+    return s;
+  if ((s = check_tensor(o, "o")) != FA_OK) return s;
+  if ((s = check_device()) != FA_OK) return s;
+  const fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
+  if (dtype == FA_DTYPE_BF16) return run_dq_prepare(p, q, k, v, o, dO, lse, dq, workspace);
+  if ((s = run_prepare(p, dtype, o, dO, lse, workspace)) != FA_OK) return s;
+  return run_dq(p, dtype, q, k, v, dO, lse, dq, workspace);
 }
 
 fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
     const T* o = O + row * D + part * 8;
     const T* g = dO + row * D + part * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sum += (float)o[e] * (float)g[e];
+    for (int e = 0; e < 8; ++e) sum = fmaf((float)o[e], (float)g[e], sum);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);

@@ -44,8 +44,9 @@ constexpr int kDqBc = 64;                         // keys per tile
 template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                                                        const float* __restrict__ LSE2,
-                                                        const float* __restrict__ DELTA, __bf16* __restrict__ dQ,
+                                                        float* __restrict__ LSE2, float* __restrict__ DELTA,
+                                                        __bf16* __restrict__ dQ, const __bf16* __restrict__ Opre,
+                                                        const float* __restrict__ LSEpre,
                                                         int H, int N, float scale, float c_log2,
                                                         const int32_t* __restrict__ seqlens,
                                                         const uint8_t* __restrict__ bmask, Dropout dr, int nqb,
@@ -139,8 +140,39 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     qf[ds] = *(const bf16x8*)(Qh + (int64_t)qrow * D + 16 * ds + 8 * half);
     gf[ds] = *(const bf16x8*)(dOh + (int64_t)qrow * D + 16 * ds + 8 * half);
   }
-  float lse2 = LSE2[row0 + qrow];        // LSE log2(e) of this lane's query
-  float del = DELTA[row0 + qrow];        // D = sum_c dO_c O_c
+  float lse2, del;  // LSE log2(e) and D = sum_c dO_c O_c of this lane's query
+  if (Opre == nullptr) {
+    lse2 = LSE2[row0 + qrow];
+    del = DELTA[row0 + qrow];
+  } else {
+    // The prepare stage folded in: D from this lane's dO fragments and the same fragments of O, summed
+    // in the prepare kernel's order (8 products per part of 8 columns, part p = 2 ds + half, then a tree
+    // over the parts: p ^ 8 .. p ^ 2 in the lane, p ^ 1 across the lane halves), so it is bitwise
+    // what that kernel writes; stored for the dK/dV pass with LSE log2(e).
+    float sp[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 of = *(const bf16x8*)(Opre + (row0 + qrow) * D + 16 * ds + 8 * half);
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaf((float)of[e], (float)gf[ds][e], a);
+      sp[ds] = a;
+    }
+#pragma unroll
+    for (int st = DS / 2; st >= 1; st >>= 1) {
+      float t[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) t[ds] = sp[ds] + sp[ds ^ st];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) sp[ds] = t[ds];
+    }
+    del = add_halves(sp[0]);
+    lse2 = LSEpre[row0 + qrow] * kLog2e;
+    if (half == 0 && query < N) {
+      DELTA[row0 + query] = del;
+      LSE2[row0 + query] = lse2;
+    }
+  }
 
   f32x16 acc[DT];  // dQ^T [d][q]: lane = query column, rows d = 32 dt + 8 (r/4) + 4 half + r%4
 #pragma unroll
@@ -330,8 +362,9 @@ hipError_t launch(const Problem& p, const void* q, const void* k, const void* v,
   const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE, DROP>), dim3((unsigned)(nqb * BH)),
                      dim3(kDqWaves * 64), 0, p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)dO, lse2, delta, (__bf16*)dq, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens,
-                     p.block_mask, dr, nqb, BH);
+                     (const __bf16*)dO, const_cast<float*>(lse2), const_cast<float*>(delta), (__bf16*)dq,
+                     (const __bf16*)p.pre_o, p.pre_lse, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, p.block_mask,
+                     dr, nqb, BH);
   return hipGetLastError();
 }
 

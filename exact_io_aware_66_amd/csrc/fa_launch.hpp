@@ -21,6 +21,10 @@ struct Problem {
   uint32_t drop_t = 256;                // keep threshold round((1 - p) 256)
   float fp8_qk_descale = 1.f;           // FP8 forward: descale(Q) descale(K), folded into the score scale
   float fp8_v_descale = 1.f;            // FP8 forward: descale(V), applied to O
+  // dQ pass that also forms the row statistics (the prepare stage folded in): O and the forward's
+  // LSE, or nullptr when the workspace already holds D and LSE log2(e)
+  const void* pre_o = nullptr;
+  const float* pre_lse = nullptr;
 };
 
 // Workspace carve-up of the backward (byte offsets; all 256-byte aligned).
@@ -46,6 +50,8 @@ hipError_t launch_bwd_prepare(const Problem& p, bool bf16, const void* o, const 
                               void* workspace);
 hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                                 void* dk, void* dv, const void* workspace);
+// With p.pre_o set, the dQ pass also writes D and LSE log2(e) of its rows into the workspace, bitwise equal
+// to what launch_bwd_prepare writes.
 hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO, void* dq,
                               const void* workspace);
 hipError_t launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v, const float* dO,

@@ -101,8 +101,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The backward in its three stages, for callers that schedule or time them separately.
- * fa_backward(...) is exactly these three calls in order on one stream, with the same workspace:
+ * The backward in its stages, for callers that schedule or time them separately.  fa_backward(...)
+ * gives the results of these three calls in order on one stream, with the same workspace:
  *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; for bf16 also LSE_i log2(e).
  *                         Reads o, dO and lse only.
  *   fa_backward_dkdv    : the recompute pass over query blocks for each block of keys: writes dk
@@ -111,6 +111,12 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
  *                         Reads the workspace as fa_backward_prepare left it.
  * fa_backward_dkdv and fa_backward_dq do not depend on each other (both only read the workspace),
  * so they may run in either order or on two streams once fa_backward_prepare has completed.
+ *   fa_backward_dq_prepare : fa_backward_prepare and fa_backward_dq in one call (it also reads o):
+ *                         writes dq and leaves in the workspace exactly what fa_backward_prepare
+ *                         writes, so fa_backward_dkdv may follow it.  For bf16 one pass forms D and
+ *                         LSE log2(e) of each row from the rows of o and dO it holds anyway, summed in
+ *                         the prepare stage's order (bitwise the same values); fa_backward runs it,
+ *                         then fa_backward_dkdv, for dense bf16 attention.
  * Arguments, layout and errors as in fa_backward.
  */
 fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -123,6 +129,11 @@ fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const vo
                            void* dq, int B, int H, int N, int d, float scale, int causal,
                            const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
                            size_t workspace_bytes, void* stream);
+fa_status_t fa_backward_dq_prepare(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dO, const float* lse, void* dq, int B, int H, int N,
+                                   int d, float scale, int causal, const int32_t* seqlens,
+                                   fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * Block-sparse attention: the computation above restricted to a pattern of 128 x 128 blocks.

@@ -152,7 +152,7 @@ def test_determinism(fa):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_backward_stages(fa, dtype):
     """prepare + dkdv + dq equals fa_backward bitwise, in either order of the last two, whatever the
-    workspace held before."""
+    workspace held before; so does dq_prepare + dkdv, whose workspace equals the prepare stage's."""
     x = workloads.draw_custom(2, 3, 300, 128, dtype=dtype, causal=True, seqlens=[300, 171], seed=5)
     _say(f"[parity] backward stages {dtype}")
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
@@ -175,6 +175,21 @@ def test_backward_stages(fa, dtype):
         torch.cuda.synchronize()
         for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
             assert torch.equal(got, want), (order, name)
+    # the dQ pass with the prepare stage folded in leaves the prepare stage's workspace, bitwise, and
+    # with the dK/dV pass after it gives fa_backward's results
+    ws.fill_(0xFF)
+    fa.fa_backward_prepare(o, do, lse, ws)
+    torch.cuda.synchronize()
+    ws_prepared = ws.clone()
+    ws.fill_(0xFF)
+    dq, dk, dv = torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)
+    fa.fa_backward_dq_prepare(q, k, v, o, do, lse, dq, x["scale"], True, sl, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, ws_prepared), "workspace after fa_backward_dq_prepare"
+    fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, x["scale"], True, sl, ws)
+    torch.cuda.synchronize()
+    for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        assert torch.equal(got, want), ("dq_prepare", name)
 
 
 def test_no_device_allocation(fa):
