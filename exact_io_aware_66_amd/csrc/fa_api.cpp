@@ -265,8 +265,9 @@ fa_status_t backward_impl(const void* q, const void* k, const void* v, const voi
   fa::Problem p = problem(B, H, N, d, scale, causal, seqlens, stream);
   p.block_mask = block_mask;
   set_dropout(p, drop, t);
-  if (dtype == FA_DTYPE_BF16 && !drop.on && block_mask == nullptr) {
-    // dense bf16: the dQ pass forms the row statistics itself, then the dK/dV pass reads them
+  if (dtype == FA_DTYPE_BF16) {
+    // bf16: the dQ pass forms the row statistics itself (every query row has its dQ workgroup, whatever
+    // the block mask or dropout), then the dK/dV pass reads them
     if ((s = run_dq_prepare(p, q, k, v, o, dO, lse, dq, workspace)) != FA_OK) return s;
     return run_dkdv(p, dtype, q, k, v, dO, lse, dk, dv, workspace);
   }

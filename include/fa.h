@@ -115,8 +115,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
  *                         writes dq and leaves in the workspace exactly what fa_backward_prepare
  *                         writes, so fa_backward_dkdv may follow it.  For bf16 one pass forms D and
  *                         LSE log2(e) of each row from the rows of o and dO it holds anyway, summed in
- *                         the prepare stage's order (bitwise the same values); fa_backward runs it,
- *                         then fa_backward_dkdv, for dense bf16 attention.
+ *                         the prepare stage's order (bitwise the same values); fa_backward (and the
+ *                         block-sparse and dropout backwards) run it, then the dK/dV pass, for bf16.
  * Arguments, layout and errors as in fa_backward.
  */
 fa_status_t fa_backward_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
