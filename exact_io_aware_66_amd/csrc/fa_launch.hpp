@@ -45,7 +45,8 @@ hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const
 hipError_t launch_fwd_fp8(const Problem& p, const void* q8, const void* k8, const void* v8, void* o, float* lse);
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v, float* o, float* lse);
 // Backward stages.  prepare: D (and, for bf16, LSE log2 e) into the workspace; dkdv: dK and dV;
-// dq: dQ.  dkdv and dq read the workspace that prepare wrote and are independent of each other.
+// dq: dQ.  dkdv and dq read the workspace that prepare wrote and are independent of each other; a dQ
+// launch with p.pre_o set writes that workspace itself (so it must precede dkdv).
 hipError_t launch_bwd_prepare(const Problem& p, bool bf16, const void* o, const void* dO, const float* lse,
                               void* workspace);
 hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
