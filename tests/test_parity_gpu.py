@@ -207,3 +207,36 @@ def test_no_device_allocation(fa):
     torch.cuda.synchronize()
     assert torch.cuda.memory_allocated() == alloc0
     assert torch.cuda.mem_get_info()[0] == free0
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 40, 1000, True), (1, 40, 1000, False), (2, 36, 500, True),
+                                          (2, 16, 4096, True)])
+def test_dkdv_batched_equals_per_head(fa, B, H, N, causal):
+    """dK and dV of a many-head problem (several key blocks per compute unit, XCD-grouped order) equal
+    bit for bit those of each head run as a problem of its own (one key block per workgroup, a
+    different grid and order): each key block's result depends only on its own inputs.  Head (0, 0)
+    is also checked against the oracle."""
+    x = workloads.draw_custom(B, H, N, 128, dtype="bf16", causal=causal, seed=2000 + N + H)
+    _say(f"[parity] dK/dV batched vs per head B={B} H={H} N={N} causal={causal}")
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    fa.fa_forward(q, k, v, o, lse, x["scale"], causal)
+    ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, 128, q.dtype), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, x["scale"], causal, None, ws)
+    ws1 = torch.empty(fa.fa_backward_workspace_size(1, 1, N, 128, q.dtype), dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        for h in range(H):
+            sl = [t[b:b + 1, h:h + 1].contiguous() for t in (q, k, v, o, do)]
+            g = [torch.empty_like(sl[0]) for _ in range(3)]
+            fa.fa_backward(*sl, lse[b:b + 1, h:h + 1].contiguous(), *g, x["scale"], causal, None, ws1)
+            torch.cuda.synchronize()
+            assert torch.equal(g[0][0, 0], dq[b, h]), ("dq", b, h)
+            assert torch.equal(g[1][0, 0], dk[b, h]), ("dk", b, h)
+            assert torch.equal(g[2][0, 0], dv[b, h]), ("dv", b, h)
+    one = {n: x[n][:1, :1] for n in ("q", "k", "v", "do")}
+    one.update(scale=x["scale"], causal=causal, seqlens=None)
+    report = []
+    fails = _compare_full(one, {"dk": dk[:1, :1].cpu(), "dv": dv[:1, :1].cpu()}, report)
+    _say("\n".join(report))
+    assert not fails, fails
