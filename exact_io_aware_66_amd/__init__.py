@@ -135,6 +135,35 @@ def _same(ref, *ts):
             raise ValueError("tensors must be on one device")
 
 
+# The C ABI takes raw pointers and cannot see sizes, so these checks are the only place where a
+# tensor of the wrong shape or element type is caught before a kernel reads or writes past it.
+def _like(ref, **named):
+    """Every named tensor has ref's shape and element type (the [B, H, N, d] operands)."""
+    for name, t in named.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {ref.dtype}")
+
+
+def _lse(lse, B, H, N):
+    """The row statistic: float32 [B, H, N]."""
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        got = None if lse is None else (lse.dtype, tuple(lse.shape))
+        raise ValueError(f"lse must be float32 of shape {(B, H, N)} (got {got})")
+
+
+def _workspace(ws):
+    """Workspace bytes: a uint8 tensor (the library checks the size itself)."""
+    if ws is None:
+        return 0
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError(f"workspace must be a 1-D uint8 tensor (got {ws.dtype}, {ws.dim()}-D)")
+    return ws.numel()
+
+
 def _seqlens(seqlens, B, device):
     if seqlens is None:
         return None
@@ -165,6 +194,8 @@ def fa_forward(q, k, v, o, lse, scale: float, causal: bool = False, seqlens=None
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, lse)
+    _like(q, k=k, v=v, o=o)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
     _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
                           _ptr(seqlens), _dtype_code(q), _stream(stream)))
@@ -176,8 +207,10 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fa
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    _like(q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                            _ptr(workspace), nbytes, _stream(stream)))
@@ -188,6 +221,8 @@ def fa_forward_block_sparse(q, k, v, o, lse, scale: float, causal: bool, seqlens
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, lse)
+    _like(q, k=k, v=v, o=o)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
     block_mask = _block_mask(block_mask, B, H, N, q.device)
     _check(lib.fa_forward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
@@ -201,9 +236,11 @@ def fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale: float, caus
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    _like(q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
     block_mask = _block_mask(block_mask, B, H, N, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                         _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens),
                                         _ptr(block_mask), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
@@ -215,6 +252,8 @@ def fa_forward_dropout(q, k, v, o, lse, scale: float, causal: bool, seqlens, p: 
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, lse)
+    _like(q, k=k, v=v, o=o)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
     _check(lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                   int(bool(causal)), _ptr(seqlens), float(p), int(seed), int(offset), _dtype_code(q),
@@ -227,8 +266,10 @@ def fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: b
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    _like(q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                    B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), float(p), int(seed),
                                    int(offset), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
@@ -251,7 +292,9 @@ def fa_forward_kv_outer(q, k, v, o, lse, scale: float, lds_bytes: int, workspace
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, lse, workspace)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _like(q, k=k, v=v, o=o)
+    _lse(lse, B, H, N)
+    nbytes = _workspace(workspace)
     _check(lib.fa_forward_kv_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                    int(lds_bytes), _dtype_code(q), _ptr(workspace), nbytes, _stream(stream)))
 
@@ -265,8 +308,10 @@ def fa_forward_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: fl
     for t in (q8, k8, v8):
         if t.dtype != torch.float8_e4m3fn:
             raise FAError(2, f"FP8 inputs must be torch.float8_e4m3fn (got {t.dtype})")
-    if o.dtype != torch.bfloat16:
-        raise ValueError("o must be bfloat16")
+    _like(q8, k8=k8, v8=v8)
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != tuple(q8.shape):
+        raise ValueError(f"o must be bfloat16 of shape {tuple(q8.shape)}")
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q8.device)
     _check(lib.fa_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(descale_q), float(descale_k), float(descale_v),
                               _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens),
@@ -278,8 +323,11 @@ def fa_backward_prepare(o, do, lse, workspace, stream=None) -> None:
     lib = load()
     B, H, N, d = _dims(o)
     _same(o, do, lse, workspace)
+    _like(o, do=do)
+    _lse(lse, B, H, N)
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_prepare(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _dtype_code(o), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+                                   nbytes, _stream(stream)))
 
 
 def fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale: float, causal: bool = False, seqlens=None,
@@ -288,8 +336,10 @@ def fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale: float, causal: bool = Fals
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, do, lse, dk, dv, workspace)
+    _like(q, k=k, v=v, do=do, dk=dk, dv=dv)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
                                 B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                                 _ptr(workspace), nbytes, _stream(stream)))
@@ -301,8 +351,10 @@ def fa_backward_dq_prepare(q, k, v, o, do, lse, dq, scale: float, causal: bool =
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, o, do, lse, dq, workspace)
+    _like(q, k=k, v=v, o=o, do=do, dq=dq)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_dq_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                       B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                                       _ptr(workspace), nbytes, _stream(stream)))
@@ -314,8 +366,10 @@ def fa_backward_dq(q, k, v, do, lse, dq, scale: float, causal: bool = False, seq
     lib = load()
     B, H, N, d = _dims(q)
     _same(q, k, v, do, lse, dq, workspace)
+    _like(q, k=k, v=v, do=do, dq=dq)
+    _lse(lse, B, H, N)
     seqlens = _seqlens(seqlens, B, q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace(workspace)
     _check(lib.fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq),
                               B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                               _ptr(workspace), nbytes, _stream(stream)))

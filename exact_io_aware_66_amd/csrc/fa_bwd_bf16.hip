@@ -14,7 +14,7 @@
 //             K and V of the wave stay in registers (B operands of S = Q K^T and dP = dO V^T), and
 //             dK^T, dV^T accumulate in registers over the whole walk of query tiles (32 rows at
 //             d=128, 64 at d=64).  The query tiles (Q, dO, LSE log2 e, D) stream through a
-//             three-stage LDS ring filled by direct global->LDS loads two tiles ahead.  Per tile u,
+//             four-stage LDS ring filled by direct global->LDS loads three tiles ahead.  Per tile u,
 //             one barrier, then
 //               C: S(u+1) = Q K^T and dP(u+1) = dO V^T on the matrix cores (into the other of two
 //                  register sets), interleaved with P(u) = exp2(S scale log2 e - LSE log2 e),

@@ -9,13 +9,15 @@
 // GPU at roughly 300 G operations/s; accumulating dQ that way made the backward bound by them.)
 //
 // gfx950 design (shared with the forward kernel):
-//   * one workgroup = 4 waves = 128 query rows of one (batch, head); a wave owns 32 rows and fits
-//     in 256 registers, so two workgroups share a compute unit and cover each other's stalls;
+//   * one workgroup = 8 waves = 256 query rows of one (batch, head), one workgroup per compute unit;
+//     a wave owns 32 rows and fits in 256 registers, so two waves share each SIMD and cover each
+//     other's stalls (a build with FA_DQ_WAVES=4 makes 128-row workgroups, two per compute unit);
 //   * Q^T and dO^T of the wave stay in registers as B operands of S^T = K Q^T and dP^T = V dO^T
 //     (v_mfma_f32_32x32x16_bf16); each lane holds one query column, so LSE and D are one scalar
 //     per lane;
-//   * K and V tiles of 64 keys are double-buffered in LDS with direct buffer->LDS loads; K is read
-//     twice: row-major for S^T and through the transposing read for dQ^T += K^T dS^T;
+//   * K and V tiles of 64 keys pass through a three-stage LDS ring (two stages in the 4-wave build),
+//     fetched two tiles ahead by direct buffer->LDS loads; K is read twice: row-major for S^T and
+//     through the transposing read for dQ^T += K^T dS^T;
 //   * dS^T goes from registers straight into the B operand of the dQ^T product (the key order
 //     inside each 16-key step is permuted the same way on both operands);
 //   * tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden scores to
@@ -230,13 +232,10 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
 #pragma unroll
     for (int r = 0; r < 16; ++r) sv[r] = s[r];
     if (t >= n_full) {
-      const int key0 = t * kDqBc + 32 * kt;
+      // element r holds key key0 + 8 (r / 4) + 4 half + r % 4, visible iff below this lane's limit
+      const int lim = (CAUSAL ? min(L, query + 1) : L) - (t * kDqBc + 32 * kt + 4 * half);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = (key < L) & (!CAUSAL | (key <= query));
-        sv[r] = vis ? sv[r] * c_log2 : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3)) < lim ? sv[r] * c_log2 : -INFINITY;
       cf = 1.f;
     }
     // dropout: dP of the kept elements, scaled by 256/t; the others contribute P (0 - D)

@@ -21,7 +21,8 @@
  *                 visible only if j < clamp(seqlens[b], 0, N), for every head and every query.
  *                 Query rows at or past that length are still computed (they attend to the valid
  *                 keys).  A row with no visible key gets O = 0, LSE = -inf and no gradient.
- *   Both masks combine by AND.  There is no dropout.
+ *   Both masks combine by AND.  fa_forward and fa_backward apply no dropout; the fa_*_dropout entry
+ *   points below add it.
  *
  * Layout and types (all tensors are caller-owned device memory)
  *   q, k, v, o, dO, dq, dk, dv : contiguous row-major [B][H][N][d], d fastest, element type `dtype`.
@@ -226,10 +227,24 @@ fa_status_t fa_forward_fp8(const void* q8, const void* k8, const void* v8, float
                            float descale_v, void* o, float* lse, int B, int H, int N, int d, float scale,
                            int causal, const int32_t* seqlens, void* stream);
 
-/* Static, never-NULL description of a status code. */
+/*
+ * Error reporting.  The pages warn that an attention integration can fall back to the naive
+ * computation without saying so, and that it must be checked that the fused kernel is what runs
+ * (aicassindra FlashAttention architecture page, "The architecture: every piece explained" and
+ * "End-to-end flow"; stackzen glossary entry "FlashAttention").  This library therefore never
+ * falls back: every condition it cannot serve is a status code, and these two calls say which.
+ *
+ * fa_status_string: a static, never-NULL name of a status code ("FA_ERR_UNKNOWN" for a value
+ *   outside fa_status_t).  Thread-safe; the string is owned by the library and never freed.
+ */
 const char* fa_status_string(fa_status_t status);
 
-/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+/*
+ * fa_last_error: detail of the last non-OK status returned on the calling thread: the failed
+ *   check with the offending values, or the HIP runtime's error name and text; "" after a call
+ *   that returned FA_OK.  The buffer is thread-local, owned by the library, valid until the next
+ *   call on the same thread; never NULL.
+ */
 const char* fa_last_error(void);
 
 #ifdef __cplusplus

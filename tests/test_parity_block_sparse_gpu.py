@@ -94,3 +94,20 @@ def test_block_sparse_determinism(fa):
     runs = [run_gpu(fa, x) for _ in range(2)]
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(runs[0][name], runs[1][name]), name
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, "bf16", True), (128, "bf16", True), (128, "bf16", False),
+                                            (64, "fp32", False)])
+def test_block_sparse_negative_scale(fa, d, dtype, causal):
+    """A negative scale selects the kernels' minimum-tracking forms; their block-sparse forms against the
+    oracle with the same mask."""
+    N = 520
+    x = workloads.draw_custom(2, 2, N, d, dtype=dtype, causal=causal, seqlens=[N, 333], q_std=2.0, seed=4100 + d)
+    x["scale"] = -0.2
+    x["block_mask"] = workloads.draw_block_mask(2, 2, N, "random", density=0.6, seed=d + 1)
+    _say(f"[parity] block-sparse scale=-0.2 N={N} d={d} {dtype} causal={causal}")
+    got = run_gpu(fa, x)
+    report = []
+    fails = _compare(x, got, report)
+    _say("\n".join(report))
+    assert not fails, fails

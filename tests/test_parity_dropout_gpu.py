@@ -92,3 +92,19 @@ def test_dropout_determinism_and_offsets(fa):
     x["dropout"] = (0.3, 11, 1)
     c = run_gpu(fa, x)
     assert not torch.equal(a["o"], c["o"]) and torch.equal(a["lse"], c["lse"])  # LSE is undropped
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, "bf16", True), (128, "bf16", True), (128, "bf16", False),
+                                            (64, "fp32", True)])
+def test_dropout_negative_scale(fa, d, dtype, causal):
+    """A negative scale selects the kernels' minimum-tracking forms (the running extreme of the scores is
+    a minimum of the raw products): the dropout forms of those must match the oracle too."""
+    x = workloads.draw_custom(2, 2, 300, d, dtype=dtype, causal=causal, seqlens=[300, 211], q_std=2.0, seed=5100 + d)
+    x["scale"] = -0.2
+    x["dropout"] = (0.25, 0xBEEF + d, 2)
+    _say(f"[parity] dropout scale=-0.2 N=300 d={d} {dtype} causal={causal}")
+    got = run_gpu(fa, x)
+    report = []
+    fails = _compare(x, got, report)
+    _say("\n".join(report))
+    assert not fails, fails

@@ -12,15 +12,21 @@ from parity_util import check
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("N,mask,q_std", [(300, "none", 1.0), (1000, "causal", 4.0), (1000, "pad", 1.0),
-                                          (4096, "causal", 4.0), (129, "causal+pad", 2.0)])
-def test_fp8_forward_parity(fa, N, mask, q_std):
+@pytest.mark.parametrize("N,mask,q_std,scale", [(300, "none", 1.0, None), (1000, "causal", 4.0, None),
+                                                (1000, "pad", 1.0, None), (4096, "causal", 4.0, None),
+                                                (129, "causal+pad", 2.0, None), (300, "causal", 2.0, -0.2),
+                                                (520, "pad", 2.0, -0.2)])
+def test_fp8_forward_parity(fa, N, mask, q_std, scale):
+    """scale < 0 selects the minimum-tracking form of the kernel (the running extreme of the raw
+    products is a minimum)."""
     causal = "causal" in mask
     B, H, d = 2, 2, 128
     seqlens = [max(1, N // 2 + 3), max(1, N - 7)] if "pad" in mask else None
     x = workloads.draw_custom(B, H, N, d, dtype="fp32", causal=causal, seqlens=seqlens, q_std=q_std, seed=7000 + N)
+    if scale is not None:
+        x["scale"] = scale
     (q8, dq), (k8, dk), (v8, dv) = (workloads.quantize_fp8(x[n]) for n in ("q", "k", "v"))
-    print(f"[parity] fp8 forward N={N} mask={mask} q_std={q_std}", flush=True)
+    print(f"[parity] fp8 forward N={N} mask={mask} q_std={q_std} scale={x['scale']}", flush=True)
     o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
     sl = None if seqlens is None else x["seqlens"].cuda()

@@ -1,13 +1,20 @@
 """GPU parity: the HIP path (through the C-ABI binding) against the fp64 oracle, element by element,
 on the seeded workloads and on ragged, masked and degenerate edge cases."""
 import math
+import os
+import sys
 
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
 from parity_util import check, run_gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+sys.path.insert(0, GOLDEN)
+from make_workload5_keys import input_digest  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -39,11 +46,15 @@ def test_workload_full(fa, wid):
     assert not fails, fails
 
 
-@pytest.mark.timeout(900)
 def test_workload5_sampled(fa):
     w = workloads.WORKLOADS[5]
-    _say(f"[parity] workload 5 {w.name} sampled rows")
+    _say(f"[parity] workload 5 {w.name} sampled rows and keys, all {w.H} heads")
     x = workloads.draw(w)
+    # dK, dV on the sampled keys need LSE and D of all 65536 rows of each head: a complete fp64 oracle
+    # pass per head, stored once by tests/golden/make_workload5_keys.py (keyed to the inputs' digest)
+    gold = np.load(os.path.join(GOLDEN, "workload5_keys.npz"))
+    assert str(gold["digest"]) == input_digest(x), "stored oracle values were made from other inputs"
+    assert np.array_equal(gold["keys"], x["keys"].numpy())
     got = run_gpu(fa, x)
     report, fails = [], []
     dt = x["q"].dtype
@@ -57,13 +68,11 @@ def test_workload5_sampled(fa):
     fails += check("o", torch.stack(o_got), torch.stack(o_ref), dt, "o", report)
     fails += check("lse", torch.stack(lse_got), torch.stack(lse_ref), dt, "lse", report)
     fails += check("dq", torch.stack(dq_got), torch.stack(dq_ref), dt, "dq", report)
-    # dK, dV on the sampled keys of head 0 need LSE and D of all 65536 rows: one chunked fp64 pass.
-    keys = x["keys"][0]
-    lse_all, d_all = oracle.row_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], False, None, 0, 0, chunk=2048,
-                                      progress=lambda r, n: r % 16384 == 0 and _say(f"  oracle rows {r}/{n}"))
-    dk_r, dv_r = oracle.backward_keys(x["q"], x["k"], x["v"], x["do"], x["scale"], False, None, 0, 0, keys, lse_all, d_all)
-    fails += check("dk", got["dk"][0, 0, keys], dk_r, dt, "dk", report)
-    fails += check("dv", got["dv"][0, 0, keys], dv_r, dt, "dv", report)
+    keys = x["keys"]
+    dk_got = torch.stack([got["dk"][0, h, keys[h]] for h in range(w.H)])
+    dv_got = torch.stack([got["dv"][0, h, keys[h]] for h in range(w.H)])
+    fails += check("dk", dk_got, torch.from_numpy(gold["dk"]), dt, "dk", report)
+    fails += check("dv", dv_got, torch.from_numpy(gold["dv"]), dt, "dv", report)
     # properties at full size, every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i (every row sees a key)
     dk_sum = got["dk"].double().sum(2)
     dv_sum = got["dv"].double().sum(2)
@@ -85,8 +94,6 @@ TAILS = [1, 17, 100, 129, 300, 1000]
 @pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal+pad"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_tails_and_masks(fa, N, d, mask, dtype):
-    if dtype == "fp32" and N > 300:
-        pytest.skip("fp32 path is checked at small sizes")
     causal = "causal" in mask
     B, H = 2, 3
     seqlens = None
