@@ -15,6 +15,7 @@ missing or a call is unsupported, these functions raise.
     fa_forward_kv_outer_workspace_size(B, H, N, d)
     fa_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, o, lse, scale, causal, seqlens)
     fa_backward_block_sparse(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens, block_mask, workspace)
+    fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale, causal, seqlens)   # library-held workspace
     forward(q, k, v, ...) -> (o, lse)                               # allocating conveniences
     backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv)
 """
@@ -36,7 +37,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARGUMENT", 2: "FA_ERR_UNSUPPORTED", 3: 
 EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_prepare", "fa_backward_dkdv",
            "fa_backward_dq", "fa_backward_dq_prepare", "fa_forward_block_sparse", "fa_backward_block_sparse", "fa_forward_dropout",
            "fa_backward_dropout", "fa_dropout_mask", "fa_forward_kv_outer", "fa_forward_kv_outer_workspace_size",
-           "fa_forward_fp8", "fa_status_string", "fa_last_error")
+           "fa_forward_fp8", "fa_backward_noalloc", "fa_status_string", "fa_last_error")
+NOALLOC_WORKSPACE_BYTES = 8 * 1024 * 1024  # FA_NOALLOC_WORKSPACE_BYTES
 MASK_BLOCK = 128  # FA_MASK_BLOCK: rows and columns of one block of the block-sparse mask
 
 _lib = None
@@ -87,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.fa_forward_kv_outer_workspace_size.restype = sz
     lib.fa_forward_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp, vp]
     lib.fa_forward_fp8.restype = i
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -214,6 +218,21 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fa
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens), _dtype_code(q),
                            _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, seqlens=None,
+                        stream=None) -> None:
+    """C-ABI fa_backward_noalloc: fa_backward with the library's own static workspace (nothing allocated;
+    calls that overlap in time on one GPU race)."""
+    lib = load()
+    B, H, N, d = _dims(q)
+    _same(q, k, v, o, do, lse, dq, dk, dv)
+    _like(q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
+    _lse(lse, B, H, N)
+    seqlens = _seqlens(seqlens, B, q.device)
+    _check(lib.fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens),
+                                   _dtype_code(q), _stream(stream)))
 
 
 def fa_forward_block_sparse(q, k, v, o, lse, scale: float, causal: bool, seqlens, block_mask, stream=None) -> None:

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <utility>
 
 #include "fa_launch.hpp"
@@ -111,11 +112,10 @@ fa_status_t validate_prepare(const void* o, const void* dO, const float* lse, in
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
-// Arguments shared by the two recompute stages; `outs` are the stage's outputs.
-fa_status_t validate_stage(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                           std::initializer_list<std::pair<const void*, const char*>> outs, int B, int H, int N, int d,
-                           float scale, const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
-                           size_t workspace_bytes) {
+// Arguments shared by the two recompute stages, apart from the workspace; `outs` are the stage's outputs.
+fa_status_t validate_stage_args(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                                std::initializer_list<std::pair<const void*, const char*>> outs, int B, int H, int N,
+                                int d, float scale, const int32_t* seqlens, fa_dtype_t dtype) {
   fa_status_t s;
   if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
   if ((s = check_tensor(q, "q")) != FA_OK || (s = check_tensor(k, "k")) != FA_OK || (s = check_tensor(v, "v")) != FA_OK ||
@@ -126,7 +126,15 @@ fa_status_t validate_stage(const void* q, const void* k, const void* v, const vo
   if (seqlens != nullptr && !aligned(seqlens, 4)) return fail(FA_ERR_MISALIGNED, "seqlens is not 4-byte aligned");
   if (dtype == FA_DTYPE_BF16 && (fa::bwd_dkdv_bf16_grid(B, H, N) > 0x7fffffff || fa::bwd_dq_bf16_grid(B, H, N) > 0x7fffffff))
     return fail(FA_ERR_INVALID_ARGUMENT, "B*H*ceil(N/128) must be below 2^31");
-  if ((s = check_head_bytes(N, d, dtype)) != FA_OK) return s;
+  return check_head_bytes(N, d, dtype);
+}
+
+fa_status_t validate_stage(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           std::initializer_list<std::pair<const void*, const char*>> outs, int B, int H, int N, int d,
+                           float scale, const int32_t* seqlens, fa_dtype_t dtype, const void* workspace,
+                           size_t workspace_bytes) {
+  fa_status_t s;
+  if ((s = validate_stage_args(q, k, v, dO, lse, outs, B, H, N, d, scale, seqlens, dtype)) != FA_OK) return s;
   return check_workspace(B, H, N, d, dtype, workspace, workspace_bytes);
 }
 
@@ -466,6 +474,66 @@ fa_status_t fa_backward_dq(const void* q, const void* k, const void* v, const vo
     return s;
   if ((s = check_device()) != FA_OK) return s;
   return run_dq(problem(B, H, N, d, scale, causal, seqlens, stream), dtype, q, k, v, dO, lse, dq, workspace);
+}
+
+}  // extern "C"
+
+// ---- fa_backward_noalloc: the backward with a workspace the library holds itself, for callers that
+// cannot allocate device memory.  The workspace is a file-scope device array (one copy per GPU,
+// alive until the process ends).  In host code the array's name is only a stand-in: its device
+// address, which differs per GPU, comes from hipGetSymbolAddress on the first call with that
+// device current, and only that address is ever passed to a kernel.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (resolved once per device).
+fa_status_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                float scale, int causal, const int32_t* seqlens, fa_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  fa_status_t s;
+  if ((s = check_common(B, H, N, d, scale, dtype)) != FA_OK) return s;
+  const size_t need = fa_backward_workspace_size(B, H, N, d, dtype);
+  if (need > (size_t)FA_NOALLOC_WORKSPACE_BYTES)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_backward_noalloc: B*H*N = %lld rows need %zu bytes of workspace, more than its %d; use fa_backward",
+                (long long)B * H * N, need, FA_NOALLOC_WORKSPACE_BYTES);
+  // every other argument is validated as for fa_backward before the device is asked for the workspace,
+  // so an argument error is reported without any device call
+  if ((s = validate_stage_args(q, k, v, dO, lse, {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}}, B, H, N, d, scale, seqlens,
+                               dtype)) != FA_OK)
+    return s;
+  if ((s = check_tensor(o, "o")) != FA_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != FA_OK) return s;
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, nullptr, dtype, ws, need,
+                       stream);
 }
 
 }  // extern "C"

@@ -228,6 +228,25 @@ fa_status_t fa_forward_fp8(const void* q8, const void* k8, const void* v8, float
                            int causal, const int32_t* seqlens, void* stream);
 
 /*
+ * The backward without a caller workspace, for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as fa_backward, minus workspace and workspace_bytes: the workspace is a
+ * device array of FA_NOALLOC_WORKSPACE_BYTES held by the library, one per GPU, alive until the
+ * process ends (its address on each GPU is resolved on the first call there).  Nothing is
+ * allocated by the call.  Limit: fa_backward_workspace_size(B, H, N, d, dtype) must not exceed
+ * FA_NOALLOC_WORKSPACE_BYTES (for bf16, B*H*N <= 1048576 rows; fp32, 2097152), else
+ * FA_ERR_UNSUPPORTED before anything is enqueued.  Calls on one GPU share that array: two calls
+ * whose work overlaps in time on the same GPU (different streams, or different host threads) race
+ * and give undefined results; calls ordered on one stream do not.  The array needs no clearing:
+ * every call writes each workspace value before reading it.
+ */
+#define FA_NOALLOC_WORKSPACE_BYTES (8 * 1024 * 1024)
+fa_status_t fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                int B, int H, int N, int d, float scale, int causal,
+                                const int32_t* seqlens, fa_dtype_t dtype, void* stream);
+
+/*
  * Error reporting.  The pages warn that an attention integration can fall back to the naive
  * computation without saying so, and that it must be checked that the fused kernel is what runs
  * (aicassindra FlashAttention architecture page, "The architecture: every piece explained" and

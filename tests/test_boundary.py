@@ -211,3 +211,32 @@ def test_fp8_argument_errors(lib, kw, code):
 @pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
 def test_fp8_valid_arguments_without_device_report_hip_error(lib):
     assert _fp8(lib) == HIP
+
+
+def _bwd_na(lib, B=2, H=3, N=100, d=64, dtype=BF16, dq=P + 20480, lse=P + 16384):
+    return lib.fa_backward_noalloc(P, P + 4096, P + 8192, P + 12288, P + 24576, lse, dq, P + 28672, P + 32768,
+                                   B, H, N, d, 0.125, 1, None, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=None), INVALID), (dict(dq=P + 4), MISALIGNED), (dict(lse=None), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(N=0), INVALID),
+    # the library's workspace holds 8 MiB: 1048576 bf16 rows (8 bytes each), 2097152 fp32 rows (4 bytes)
+    (dict(B=1, H=16, N=65537), UNSUPPORTED), (dict(B=2, H=8, N=131073, dtype=F32), UNSUPPORTED),
+])
+def test_noalloc_backward_argument_errors(lib, kw, code):
+    assert _bwd_na(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_noalloc_limit_is_the_documented_one(lib):
+    assert fa.NOALLOC_WORKSPACE_BYTES == 8 * 1024 * 1024
+    assert lib.fa_backward_workspace_size(1, 16, 65536, 128, BF16) <= fa.NOALLOC_WORKSPACE_BYTES
+    assert lib.fa_backward_workspace_size(1, 16, 65537, 128, BF16) > fa.NOALLOC_WORKSPACE_BYTES
+    assert lib.fa_backward_workspace_size(1, 32, 65536, 64, F32) <= fa.NOALLOC_WORKSPACE_BYTES
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid arguments with fake pointers would launch on a GPU")
+def test_noalloc_valid_arguments_without_device_report_hip_error(lib):
+    assert _bwd_na(lib) == HIP
+    assert _bwd_na(lib, B=1, H=16, N=65536, d=128) == HIP  # the largest bf16 problem it takes
