@@ -5,11 +5,13 @@
     python bench.py --all-configs      (every workload, its fraction of the per-config roofline)
     python bench.py --naive-torch      (the materialising attention as plain torch ops; context)
 
-One step = one forward (fa_forward) plus one backward (fa_backward_dq_prepare, then fa_backward_dkdv:
-exactly what fa_backward runs for dense bf16) over one batch of the synthetic workload,
-inputs resident in HBM.  The whole-job time (`value`, `ms_per_step`) comes from K steps with no event
-between the kernels; a second run of K steps with an event around every launch gives each kernel's
-average duration (an event recorded between two kernels costs the stream a few microseconds).  Under
+One step = one forward (fa_forward) plus one backward (fa_backward) over one batch of the synthetic
+workload, inputs resident in HBM.  The whole-job time (`value`, `ms_per_step`) comes from K steps of
+those two public calls with no event between them; a second run of K steps with an event around
+every launch (the forward, then fa_backward's two stages, fa_backward_dq_prepare and
+fa_backward_dkdv, called separately: the same kernels fa_backward launches for dense bf16) gives each
+kernel's average duration (an event recorded between two kernels costs the stream a few
+microseconds).  Under
 sustained load the GPU's power management needs about a third of a
 second to reach its steady state: the clocks ramp up over the first tens of milliseconds, and about
 0.27 s in, a one-time throttle stalls the queue for ~60 ms and runs the next ~50 ms at reduced
@@ -142,6 +144,46 @@ def min_bytes(w):
     t = w.B * w.H * w.N * w.d * es
     rows = w.B * w.H * w.N
     return 4 * t + 4 * rows, 8 * t + 12 * rows
+
+
+def as_tiled_bytes(w, x):
+    """HBM bytes per launch of each bf16 kernel if every tile it loads came from HBM (no reuse between
+    workgroups in any cache): the Theta(N^2 d^2 / M) term of the pages' IO analysis for the tiles these
+    kernels actually use, next to the counters.  Forward: one workgroup per query block of B_r rows
+    (256 at d = 128, 128 at d = 64) reads its Q block once and, for every visible 64-key tile, K and V
+    (2 d bf16 values per key); O and LSE written once.  dK/dV: one workgroup per 128 keys reads its K
+    and V once and, for every visible query row, Q, dO (2 d values) and the two row statistics (8 B);
+    dK and dV written once.  dQ (with the row statistics formed in it): one workgroup per 256 query
+    rows reads its Q, dO and O rows and LSE once and, for every visible 64-key tile, K and V; dQ, D
+    and LSE log2(e) written once.  Key padding is ignored in the tile counts (an upper bound)."""
+    es = 2 if w.dtype == "bf16" else 4
+    rows = w.B * w.H * w.N
+    row_b = w.d * es
+    lens = [w.N] * w.B if x["seqlens"] is None else [max(0, min(w.N, int(s))) for s in x["seqlens"]]
+
+    def kv_tiles(br, bc=64):
+        """(visible keys, rounded up to whole tiles) summed over the query blocks of every head."""
+        total = 0
+        for L in lens:
+            for qb in range(-(-w.N // br)):
+                end = min(L, (qb + 1) * br) if w.causal else L
+                total += -(-end // bc) * bc
+        return total * w.H
+
+    def q_rows_per_key_block(bk=128):
+        total = 0
+        for L in lens:
+            for kb in range(-(-w.N // bk)):
+                if kb * bk >= L:
+                    continue
+                total += (w.N - kb * bk) if w.causal else w.N
+        return total * w.H
+
+    br_f = 256 if w.d == 128 else 128
+    fwd = rows * row_b + kv_tiles(br_f) * 2 * row_b + rows * row_b + rows * 4
+    dkdv = 2 * rows * row_b + q_rows_per_key_block() * (2 * row_b + 8) + 2 * rows * row_b
+    dq = 3 * rows * row_b + rows * 4 + kv_tiles(256) * 2 * row_b + rows * row_b + 8 * rows
+    return {"fwd_bf16_kernel": fwd, "bwd_dkdv_kernel": dkdv, "bwd_dq_kernel": dq}
 
 
 def naive_torch_forward(w, x, steps: int):
@@ -386,13 +428,18 @@ def measure(fa, w, x, steps: int, warmup: int, settle_ms: float, cold: bool = Fa
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(e=None):
-        if e: e[0].record(stream)
+        if e is None:  # the public calls
+            fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
+            fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, scale, causal, sl, ws)
+            return
+        # fa_backward's two kernels, called as its stages so that an event can separate them
+        e[0].record(stream)
         fa.fa_forward(q, k, v, o, lse, scale, causal, sl)
-        if e: e[1].record(stream)
+        e[1].record(stream)
         fa.fa_backward_dq_prepare(q, k, v, o, do, lse, dq, scale, causal, sl, ws)
-        if e: e[2].record(stream)
+        e[2].record(stream)
         fa.fa_backward_dkdv(q, k, v, do, lse, dk, dv, scale, causal, sl, ws)
-        if e: e[3].record(stream)
+        e[3].record(stream)
 
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
@@ -560,6 +607,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                      "ms_per_launch": round(dom_ms, 4)},
+        "bytes_per_launch": {"as_tiled_no_reuse": as_tiled_bytes(w, x),
+                             "counters": {kn: measured_traffic(kn, w.name) for kn in kernels},
+                             "minimum_fwd_bwd": min_bytes(w)},
     }
     if not args.no_fp8 and w.d == 128:
         out["fp8_forward"] = measure_fp8_forward(fa, w, x, args.steps, ms_fwd)

@@ -23,3 +23,30 @@ def test_block_pairs_match_element_count(N, causal, lens):
 @pytest.mark.parametrize("N,causal,L", [(4096, True, 4096), (512, False, 300), (1000, True, 611), (7, True, 0)])
 def test_visible_pairs_match_element_count(N, causal, L):
     assert bench.visible_pairs(N, causal, L) == int(oracle.visible(N, causal, L).sum())
+
+
+def _brute_kv_tiles(N, causal, L, br, bc=64):
+    """Key tiles with at least one visible (query, key) pair, counted pair by pair per query block."""
+    n = 0
+    for q0 in range(0, N, br):
+        for k0 in range(0, N, bc):
+            if any((k < L) and (not causal or k <= q) for q in range(q0, min(N, q0 + br)) for k in range(k0, min(N, k0 + bc))):
+                n += 1
+    return n
+
+
+def test_as_tiled_bytes_matches_a_brute_force_tile_count():
+    import bench
+    import workloads
+    for N, d, causal in ((512, 128, True), (300, 64, False), (640, 64, True)):
+        x = workloads.draw_custom(2, 3, N, d, dtype="bf16", causal=causal, seed=1)
+        w = workloads.Workload(0, "t", 2, 3, N, d, "bf16", causal, False)
+        got = bench.as_tiled_bytes(w, x)
+        rows, rb = 2 * 3 * N, 2 * d
+        br = 256 if d == 128 else 128
+        kv = _brute_kv_tiles(N, causal, N, br) * 64 * 2 * rb * 6
+        assert got["fwd_bf16_kernel"] == 2 * rows * rb + 4 * rows + kv
+        kvq = _brute_kv_tiles(N, causal, N, 256) * 64 * 2 * rb * 6
+        assert got["bwd_dq_kernel"] == 4 * rows * rb + 12 * rows + kvq
+        qrows = sum(sum(1 for q in range(N) if not causal or q >= k0) for k0 in range(0, N, 128)) * 6
+        assert got["bwd_dkdv_kernel"] == 4 * rows * rb + qrows * (2 * rb + 8)
