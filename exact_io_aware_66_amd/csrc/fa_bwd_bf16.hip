@@ -342,12 +342,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         for (int x = 0; x < HALF; ++x)
           if (x * steps / HALF == step) unit(base + x / 5, x % 5);
       };
-      auto valu_c = [&](int ds) { spread(0, ds, DS); };
-      // (after the last tile the product reads a stale or unwritten stage; its result is unused)
-      scores(std::integral_constant<int, 1 - P>{}, nxt, valu_c);
-
-      // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read), k-steps
-      // of queries outermost
+      // B-phase operands: dO^T and Q^T of tile u through the transposing read, kRB steps ahead in a
+      // ring; the first kRB are read during the last two k-steps of the score products, so the
+      // matrix cores do not wait for them at the phase change
       constexpr int BS = DT * 2 * QS;  // steps (ks, dt) of 2 MFMAs
       bf16x8 bd[kRB + 1], bq[kRB + 1];
       auto rdb = [&](int i, bf16x8& d, bf16x8& q) {
@@ -357,8 +354,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
         d = cat(lds_read_tr(cur + QTILE, tb0), lds_read_tr(cur + QTILE, tb8));
         q = cat(lds_read_tr(cur, tb0), lds_read_tr(cur, tb8));
       };
+      auto valu_c = [&](int ds) {
+        spread(0, ds, DS);
+        if (ds == DS - 2) {
 #pragma unroll
-      for (int i = 0; i < kRB && i < BS; ++i) rdb(i, bd[i], bq[i]);
+          for (int i = 0; i < kRB && i < BS; ++i) rdb(i, bd[i], bq[i]);
+        }
+      };
+      // (after the last tile the product reads a stale or unwritten stage; its result is unused)
+      scores(std::integral_constant<int, 1 - P>{}, nxt, valu_c);
+
+      // ---- B: dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transposing read), k-steps
+      // of queries outermost
 #pragma unroll
       for (int i = 0; i < BS; ++i) {
         __builtin_amdgcn_sched_barrier(0);

@@ -349,27 +349,31 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // O^T += V^T P^T for k-steps [ks0, ks0 + 2) of the tile in vb, k-step outermost: 2 DT MFMAs.  V^T
-  // fragment for (dt, ks): lane (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and
+  // O^T += V^T P^T over the tile in vb, k-step outermost: 4 DT MFMAs.  V^T fragment of product i
+  // (dt = i % DT, ks = i / DT): lane (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and
   // 16 ks + 8 + 4 half + 0..3, the key order of pn; two transposing reads supply them (bases for
-  // rows vrow and vrow + 8, compile-time offsets of 16 rows).  `between(i)` follows MFMA i.
-  auto pv = [&](const FA_LDS char* vb, int ks0, auto&& between) __attribute__((always_inline)) {
-    constexpr int NS = 2 * DT;
-    bf16x8 vf[3];
-    auto rd = [&](int i, bf16x8& f) {
-      const int ks = ks0 + i / DT, dt = i % DT;
-      const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
-      const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
-      f = cat(lds_read_tr(vb, off0), lds_read_tr(vb, off8));
-    };
-    rd(0, vf[0]);
-    rd(1, vf[1]);
+  // rows vrow and vrow + 8, compile-time offsets of 16 rows).  The fragments run two products ahead
+  // in a ring of three; the first two are read by the caller during the score products before it
+  // (pv_head), so the matrix cores do not wait for them at the phase change.  `between(i)` follows
+  // MFMA i.
+  constexpr int NPV = 4 * DT;
+  bf16x8 vf[3];
+  auto pv_rd = [&](const FA_LDS char* vb, int i) __attribute__((always_inline)) {
+    const int ks = i / DT, dt = i % DT;
+    const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+    const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
+    vf[i % 3] = cat(lds_read_tr(vb, off0), lds_read_tr(vb, off8));
+  };
+  auto pv_head = [&](const FA_LDS char* vb) __attribute__((always_inline)) {
+    pv_rd(vb, 0);
+    pv_rd(vb, 1);
+  };
+  auto pv = [&](const FA_LDS char* vb, auto&& between) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < NS) rd(i + 2, vf[(i + 2) % 3]);
-      const int ks = ks0 + i / DT, dt = i % DT;
-      acc[dt] = mfma32x32x16(vf[i % 3], pn[ks], acc[dt]);
+      if (i + 2 < NPV) pv_rd(vb, i + 2);
+      acc[i % DT] = mfma32x32x16(vf[i % 3], pn[i / DT], acc[i % DT]);
       between(i);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -454,9 +458,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
   // Iteration t (every wave runs t = 0 .. ntiles-1, one barrier each; V(t) and K(t+1) were loaded
   // one iteration ahead).  S(t) is in s[t % 2] (scaled and masked in place when tile t has hidden
   // pairs, else raw: cf tells which), and the maximum for P(t) is settled.
-  //   phase 1:  S(t+1) = K(t+1) Q^T into the other set  ||  P(t), k-steps 0..2
-  //   phase 2a: O += V(t)^T P(t), k-steps 0, 1           ||  P(t), k-step 3; extreme of S(t+1), first half
-  //   phase 2b: O += V(t)^T P(t), k-steps 2, 3           ||  extreme of S(t+1), second half
+  //   phase 1:  S(t+1) = K(t+1) Q^T into the other set  ||  P(t), k-steps 0..2; first V(t)^T fragments
+  //   phase 2:  O += V(t)^T P(t), k-steps 0 .. 3          ||  P(t), k-step 3, then the extreme of S(t+1)
   //   then the lazy check for tile t+1 (raise the maximum, rescale O and l), or, when tile t+1 has
   //   hidden pairs, its mask and exact update.
   // The forms differ in the next tile (fully visible, with hidden pairs, none) and in whether the
@@ -482,7 +485,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
       }
       return;
     } else {
-      // phase 1: 12 P units over the DS k-steps of S(t+1) (P only when there is no next tile)
+      // phase 1: 12 P units over the DS k-steps of S(t+1) (P only when there is no next tile); the
+      // first V^T fragments of phase 2 are read two k-steps before its end
       auto ph1 = [&](int ds) {
 #pragma unroll
         for (int x = 0; x < 12; ++x)
@@ -491,6 +495,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
             if (x == 8) dunit(t, 1);
             punit(cur, x / 4, x % 4, cf);
           }
+        if (ds == DS - 2) pv_head(vbuf[cur]);
       };
       if constexpr (NEXT != kNextNone) {
         scores(nxt, kbuf[nxt], ph1);
@@ -498,24 +503,28 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) ph1(ds);
       }
-      // phase 2a: 2 DT MFMAs; 4 P units then 4 extreme units
-      pv(vbuf[cur], 0, [&](int i) {
+      // phase 2: 4 DT MFMAs; in the first half 4 P units then 4 extreme units, in the second half 4
+      // extreme units
+      pv(vbuf[cur], [&](int i) {
+        if (i < 2 * DT) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          if (x * 2 * DT / 8 == i) {
-            if (x < 4) punit(cur, 3, x, cf);
-            else if (NEXT == kNextClean) xunit(nxt, x - 4);
-          }
-      });
-      // phase 2b: 2 DT MFMAs; 4 extreme units
-      pv(vbuf[cur], 2, [&](int i) {
+          for (int x = 0; x < 8; ++x)
+            if (x * 2 * DT / 8 == i) {
+              if (x < 4) punit(cur, 3, x, cf);
+              else if (NEXT == kNextClean) xunit(nxt, x - 4);
+            }
+        } else {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          if (x * 2 * DT / 4 == i && NEXT == kNextClean) xunit(nxt, 4 + x);
+          for (int x = 0; x < 4; ++x)
+            if (x * 2 * DT / 4 == i - 2 * DT && NEXT == kNextClean) xunit(nxt, 4 + x);
+        }
       });
       if constexpr (NEXT == kNextClean) {
-        const float tm = (NEG ? min_halves(ext) : max_halves(ext)) * c_log2;
-        if (__builtin_amdgcn_readfirstlane(__any(tm > m_run + kLazyRescale))) {
+        // Lazy check.  c_log2 scales monotonically, so some lane's partial extreme (its half's keys)
+        // passes the threshold exactly when the extreme over both halves does: the test needs no
+        // exchange between the halves, only the (rare) raise does.
+        if (__builtin_amdgcn_ballot_w64(ext * c_log2 > m_run + kLazyRescale) != 0) {
+          const float tm = (NEG ? min_halves(ext) : max_halves(ext)) * c_log2;
           const float m_new = fmaxf(m_run, tm);
           const float alpha = fast_exp2(m_p - m_new);
           m_run = m_new;
@@ -577,6 +586,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
             if (x == 8) dunit(t, 1);
             punit(0, x / 4, x % 4, cf);
           }
+        if (ds == DS - 2) pv_head(vb_cur);
       };
       if constexpr (NEXT == kNextMasked) {
         scores(1, kb_nxt, ph1);
@@ -584,12 +594,11 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) ph1(ds);
       }
-      pv(vb_cur, 0, [&](int i) {
+      pv(vb_cur, [&](int i) {
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           if (x * 2 * DT / 4 == i) punit(0, 3, x, cf);
       });
-      pv(vb_cur, 2, [](int) {});
       if constexpr (NEXT == kNextMasked) {
         const float alpha = mask_update(1, t + 1);
         if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) rescale(alpha);
