@@ -166,7 +166,7 @@ fa_status_t run_dq(const fa::Problem& p, fa_dtype_t dtype, const void* q, const 
   return e == hipSuccess ? FA_OK : hip_fail(e, "backward dQ launch");
 }
 
-// The dQ pass with the prepare stage folded in (bf16): also writes D and LSE log2(e) into the workspace.
+// The dQ pass with the prepare stage folded in (bf16): also writes -D and LSE log2(e) into the workspace.
 fa_status_t run_dq_prepare(fa::Problem p, const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* workspace) {
   p.pre_o = o;

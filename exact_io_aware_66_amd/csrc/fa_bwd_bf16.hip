@@ -9,16 +9,17 @@
 //   dS = P * (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Kernels here:
-//   bwd_pre   D_i = sum_c dO_ic O_ic and LSE_i log2(e) (fp32) into the workspace;
+//   bwd_pre   -D_i and LSE_i log2(e) (fp32) into the workspace;
 //   bwd_dkdv  one workgroup per 128 keys of a (batch, head): 4 waves x 32 keys, one wave per SIMD.
 //             K and V of the wave stay in registers (B operands of S = Q K^T and dP = dO V^T), and
 //             dK^T, dV^T accumulate in registers over the whole walk of query tiles (32 rows at
-//             d=128, 64 at d=64).  The query tiles (Q, dO, LSE log2 e, D) stream through a
+//             d=128, 64 at d=64).  The query tiles (Q, dO, LSE log2 e, -D) stream through a
 //             four-stage LDS ring filled by direct global->LDS loads three tiles ahead.  Per tile u,
 //             one barrier, then
-//               C: S(u+1) = Q K^T and dP(u+1) = dO V^T on the matrix cores (into the other of two
-//                  register sets), interleaved with P(u) = exp2(S scale log2 e - LSE log2 e),
-//                  dS(u) = P (dP - D) and their packing to bf16 for the first half of the queries;
+//               C: S(u+1) = Q K^T and dP(u+1) - D = dO V^T - D on the matrix cores (into the
+//                  other of two register sets; the dP accumulators start from -D), interleaved with
+//                  P(u) = exp2(S scale log2 e - LSE log2 e), dS(u) = P (dP - D) and their packing
+//                  to bf16 for the first half of the queries;
 //               B: dV^T += dO^T P(u), dK^T += Q^T dS(u) (dO^T, Q^T through transposing LDS reads),
 //                  first-half queries first, interleaved with P and dS of the second half.
 //             Tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden
@@ -48,7 +49,9 @@ constexpr int kRA = FA_BWD_READ_AHEAD;
 constexpr int kRB = FA_BWD_READ_AHEAD_B;
 
 // ---------------------------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic and (bf16 path) LSE_i log2(e).  D/8 threads per row.
+// -D_i = -sum_c dO_ic O_ic and (bf16 path) LSE_i log2(e).  D/8 threads per row.  The workspace keeps
+// the negated statistic: the dK/dV pass starts its dP accumulation from it, so the products come
+// out as dP - D directly.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       const float* __restrict__ LSE, float* __restrict__ delta,
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, TPR);
   if (row < rows && part == 0) {
-    delta[row] = sum;
+    delta[row] = -sum;
     if (lse2 != nullptr) lse2[row] = LSE[row] * kLog2e;
   }
 }
@@ -231,7 +234,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
         s[P][qs] = zero16();
-        dp[P][qs] = zero16();
+        // dP starts from -D of the tile's rows (the workspace's statistic, in the accumulator layout:
+        // element 4 gq + e is query 32 qs + 8 gq + 4 half + e), so it accumulates dP - D.  With
+        // dropout it starts from -D t / 256 instead: a kept element's dP is scaled by 256 / t, which
+        // gives (256 / t) dP - D (and with t = 256 exactly the dense values).
+        const FA_LDS float* nd = (const FA_LDS float*)(st + 2 * QTILE) + 64 + 32 * qs + 4 * half;
+        const f32x4 a = *(const FA_LDS f32x4*)(nd), b = *(const FA_LDS f32x4*)(nd + 8);
+        const f32x4 c = *(const FA_LDS f32x4*)(nd + 16), d = *(const FA_LDS f32x4*)(nd + 24);
+        dp[P][qs] = __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7),
+                                            __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5,
+                                            6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        if constexpr (DROP) dp[P][qs] *= (float)dr.t * (1.f / 256.f);
       }
 #pragma unroll
       for (int ds = 0; ds < kRA && ds < DS; ++ds) rd(ds, fq[ds], fd[ds]);
@@ -301,14 +314,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
       // ---- C: S(u+1), dP(u+1) on the matrix cores || P(u), dS(u) on the VALU, then packed
       const FA_LDS float* lse_t = (const FA_LDS float*)(cur + 2 * QTILE);
       const FA_LDS float* del_t = lse_t + 64;
-      // LSE log2 e and D of the lane's 4 queries in each 8-query group gq of each 32-row half qs
-      f32x4 lse4[QS][4], del4[QS][4];
+      // LSE log2 e (and, with dropout, -D) of the lane's 4 queries in each 8-query group gq of each
+      // 32-row half qs
+      f32x4 lse4[QS][4], nd4[QS][DROP ? 4 : 1];
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           lse4[qs][gq] = *(const FA_LDS f32x4*)(lse_t + 32 * qs + 8 * gq + 4 * half);
-          del4[qs][gq] = *(const FA_LDS f32x4*)(del_t + 32 * qs + 8 * gq + 4 * half);
+          if constexpr (DROP) nd4[qs][gq] = *(const FA_LDS f32x4*)(del_t + 32 * qs + 8 * gq + 4 * half);
         }
       // work unit e of k-step ks (16 queries; e < 4: two elements of P and dS, e = 4: the packing)
       auto unit = [&](int ks, int e) {
@@ -318,15 +332,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const __bf16* __restri
           for (int h = 0; h < 2; ++h) {
             const int r = 8 * (ks & 1) + 2 * e + h;
             const float p = fast_exp2(fmaf(s[P][qs][r], cf, -lse4[qs][r >> 2][r & 3]));
-            float dpv = dp[P][qs][r];
+            float dpv = dp[P][qs][r];  // dP - D (dropout: dP - D t / 256)
             float pv = p;  // P for dV: the kept probabilities (their 256/t scale is applied to dV at the end)
             if constexpr (DROP) {
               const bool keep = ((kwt[qs][r >> 2] >> (8 * (r & 3))) & 0xFFu) < dr.t;
-              dpv = keep ? dpv * dr.scale : 0.f;
+              dpv = keep ? dpv * dr.scale : nd4[qs][r >> 2][r & 3];  // (256 / t) dP - D, or 0 - D
               pv = keep ? p : 0.f;
             }
             s[P][qs][r] = pv;
-            dp[P][qs][r] = p * (dpv - del4[qs][r >> 2][r & 3]);
+            dp[P][qs][r] = p * dpv;
           }
         } else {
           pb[ks] = pack8(s[P][qs], 8 * (ks & 1));

@@ -142,10 +142,10 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     qf[ds] = *(const bf16x8*)(Qh + (int64_t)qrow * D + 16 * ds + 8 * half);
     gf[ds] = *(const bf16x8*)(dOh + (int64_t)qrow * D + 16 * ds + 8 * half);
   }
-  float lse2, del;  // LSE log2(e) and D = sum_c dO_c O_c of this lane's query
+  float lse2, del;  // LSE log2(e) and D = sum_c dO_c O_c of this lane's query (the workspace holds -D)
   if (Opre == nullptr) {
     lse2 = LSE2[row0 + qrow];
-    del = DELTA[row0 + qrow];
+    del = -DELTA[row0 + qrow];
   } else {
     // The prepare stage folded in: D from this lane's dO fragments and the same fragments of O, summed
     // in the prepare kernel's order (8 products per part of 8 columns, part p = 2 ds + half, then a tree
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     del = add_halves(sp[0]);
     lse2 = LSEpre[row0 + qrow] * kLog2e;
     if (half == 0 && query < N) {
-      DELTA[row0 + query] = del;
+      DELTA[row0 + query] = -del;
       LSE2[row0 + query] = lse2;
     }
   }

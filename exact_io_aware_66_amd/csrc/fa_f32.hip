@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(const float* __restrict_
     if (threadIdx.x < kF32Tile) {
       const int qq = min(qt0 + (int)threadIdx.x, N - 1);
       lse_s[threadIdx.x] = LSE[row0 + qq];
-      del_s[threadIdx.x] = DELTA[row0 + qq];
+      del_s[threadIdx.x] = -DELTA[row0 + qq];  // (the workspace holds -D)
     }
     __syncthreads();
     for (int i = 0; i < kF32Tile; ++i) {
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(const float* __restrict__
     gr[r][c] = dO[(row0 + qq) * D + c];
   }
   const float lse = LSE[row0 + qrow];
-  const float del = DELTA[row0 + qrow];
+  const float del = -DELTA[row0 + qrow];  // (the workspace holds -D)
   float dq[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) dq[c] = 0.f;

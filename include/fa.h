@@ -80,7 +80,7 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* o, flo
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes: one float32 per row for
- * D_i = sum_c dO_ic O_ic, plus (bf16 only) one float32 per row for LSE_i log2(e).  Returns 0 for
+ * -D_i = -sum_c dO_ic O_ic, plus (bf16 only) one float32 per row for LSE_i log2(e).  Returns 0 for
  * invalid or unsupported sizes.  Linear in N (O(N) extra memory; NOTE-005 "Key results",
  * Theorem 1).
  */
@@ -104,7 +104,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
 /*
  * The backward in its stages, for callers that schedule or time them separately.  fa_backward(...)
  * gives the results of these three calls in order on one stream, with the same workspace:
- *   fa_backward_prepare : D_i = sum_c dO_ic O_ic into the workspace; for bf16 also LSE_i log2(e).
+ *   fa_backward_prepare : -D_i = -sum_c dO_ic O_ic into the workspace (negated: the dK/dV pass
+ *                         starts its dO V^T products from it); for bf16 also LSE_i log2(e).
  *                         Reads o, dO and lse only.
  *   fa_backward_dkdv    : the recompute pass over query blocks for each block of keys: writes dk
  *                         and dv.  Reads the workspace as fa_backward_prepare left it.
