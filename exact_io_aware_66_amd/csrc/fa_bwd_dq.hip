@@ -176,6 +176,18 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     }
   }
 
+  // The dP^T accumulators start from -D (this lane's query in all 16 elements, kept in registers for
+  // the whole walk), so the matrix cores produce dP - D and dS needs one multiply per score: -3 to
+  // -6 % dQ time.  With dropout they start from -D t / 256, so that a kept element's (256 / t) dP - D
+  // needs one multiply (and t = 256 gives the dense values bitwise).  Where the 16 registers do not
+  // fit beside the rest (d = 128 without the causal mask, which then spills), D is subtracted instead.
+  constexpr bool kNdInit = D == 64 || CAUSAL;
+  const float ndel0 = DROP ? -del * ((float)dr.t * (1.f / 256.f)) : -del;
+  f32x16 ndel16;
+  if constexpr (kNdInit && !DROP) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndel16[r] = ndel0;
+  }
   f32x16 acc[DT];  // dQ^T [d][q]: lane = query column, rows d = 32 dt + 8 (r/4) + 4 half + r%4
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
@@ -208,6 +220,19 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   // budget of two waves per SIMD; the other workgroup on the compute unit fills the gaps.
   auto half_tile = [&](int t, int kt, const FA_LDS char* kb, const FA_LDS char* vb) __attribute__((always_inline)) {
     f32x16 s = zero16(), dp = zero16();
+    if constexpr (kNdInit) {
+      if constexpr (DROP) {
+        // rebuilt for every half tile (from a value made opaque, so the splat is not hoisted out of
+        // the loop): with the dropout state beside it a persistent copy does not fit in the
+        // registers at d = 128
+        float x = ndel0;
+        asm volatile("" : "+v"(x));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = x;
+      } else {
+        dp = ndel16;
+      }
+    }
     bf16x8 fk[3], fv[3];
     auto rd = [&](int ds, bf16x8& k, bf16x8& v) {
       const uint32_t off = tile_off<D>(32 * kt + l32, 16 * ds + 8 * half);
@@ -250,8 +275,13 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
         const int r = 8 * kh + e;
         const float p = fast_exp2(fmaf(sv[r], cf, -lse2));
         float dpv = dp[r];
-        if constexpr (DROP) dpv = dropout_keep(dr, kwd[r >> 2], r & 3) ? dpv * dr.scale : 0.f;
-        d8[e] = p * (dpv - del);
+        if constexpr (kNdInit) {  // dpv = dP - D (dropout: dP - D t / 256), accumulated by the matrix cores
+          if constexpr (DROP) dpv = dropout_keep(dr, kwd[r >> 2], r & 3) ? dpv * dr.scale : -del;
+          d8[e] = p * dpv;
+        } else {
+          if constexpr (DROP) dpv = dropout_keep(dr, kwd[r >> 2], r & 3) ? dpv * dr.scale : 0.f;
+          d8[e] = p * (dpv - del);
+        }
       }
       dsb[kh] = pack8f(d8, 0);
     }
