@@ -15,9 +15,10 @@
 //   * Q^T and dO^T of the wave stay in registers as B operands of S^T = K Q^T and dP^T = V dO^T
 //     (v_mfma_f32_32x32x16_bf16); each lane holds one query column, so LSE and D are one scalar
 //     per lane;
-//   * K and V tiles of 64 keys pass through a three-stage LDS ring (two stages in the 4-wave build),
-//     fetched two tiles ahead by direct buffer->LDS loads; K is read twice: row-major for S^T and
-//     through the transposing read for dQ^T += K^T dS^T;
+//   * K and V tiles of 64 keys pass through an LDS ring filled by direct buffer->LDS loads: at
+//     d = 128 three stages fetched two tiles ahead, one barrier per tile; at d = 64 four stages
+//     filled two tiles at a time, one barrier per two tiles (the 4-wave build: two stages).  K is
+//     read twice: row-major for S^T and through the transposing read for dQ^T += K^T dS^T;
 //   * dS^T goes from registers straight into the B operand of the dQ^T product (the key order
 //     inside each 16-key step is permuted the same way on both operands);
 //   * tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden scores to
@@ -34,11 +35,16 @@ namespace {
 #ifndef FA_DQ_WAVES
 #define FA_DQ_WAVES 8
 #endif
-// 8 waves (two per SIMD) share each K/V tile and a three-stage LDS ring (96 KiB, one workgroup per
-// compute unit), so tiles are fetched two steps ahead; 4 waves use two stages and two workgroups
-// per compute unit.
+// 8 waves (two per SIMD) share each K/V tile and one workgroup occupies a compute unit; 4 waves use
+// two stages and two workgroups per compute unit.
 constexpr int kDqWaves = FA_DQ_WAVES;
-constexpr int kDqStages = kDqWaves == 8 ? 3 : 2;
+// Tiles per barrier.  d = 64 (8 waves): two, through a four-stage ring (two tiles loaded after each
+// barrier, the waves meet once per two tiles; measured -1 to -4 % dQ time at d = 64).  d = 128: one,
+// through a three-stage ring fetched two tiles ahead (the grouped loop spills there).
+template <int D>
+constexpr int dq_group() { return kDqWaves == 8 && D == 64 ? 2 : 1; }
+template <int D>
+constexpr int dq_stages() { return dq_group<D>() > 1 ? 2 * dq_group<D>() : (kDqWaves == 8 ? 3 : 2); }
 constexpr int kDqRowsPerWave = 32;
 constexpr int kDqBr = kDqWaves * kDqRowsPerWave;  // query rows per workgroup
 constexpr int kDqBc = 64;                         // keys per tile
@@ -58,15 +64,19 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   constexpr int LOADS = kDqBc * CH / (64 * kDqWaves);  // 16-byte loads per thread per tile
   constexpr int DS = D / 16;               // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;               // 32-wide d tiles of dQ^T
-  // Separate, statically referenced stages (K and V of tile t in stage t % kDqStages)
+  // Separate, statically referenced stages (K and V of tile t in stage t % dq_stages<D>())
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[TILE];
-  __shared__ __attribute__((aligned(1024))) char kbuf2_raw[kDqStages > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char kbuf2_raw[dq_stages<D>() > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char kbuf3_raw[dq_stages<D>() > 3 ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) char vbuf0_raw[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1_raw[TILE];
-  __shared__ __attribute__((aligned(1024))) char vbuf2_raw[kDqStages > 2 ? TILE : 16];
-  FA_LDS char* const kst[3] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw, (FA_LDS char*)kbuf2_raw};
-  FA_LDS char* const vst[3] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw, (FA_LDS char*)vbuf2_raw};
+  __shared__ __attribute__((aligned(1024))) char vbuf2_raw[dq_stages<D>() > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char vbuf3_raw[dq_stages<D>() > 3 ? TILE : 16];
+  FA_LDS char* const kst[4] = {(FA_LDS char*)kbuf0_raw, (FA_LDS char*)kbuf1_raw, (FA_LDS char*)kbuf2_raw,
+                               (FA_LDS char*)kbuf3_raw};
+  FA_LDS char* const vst[4] = {(FA_LDS char*)vbuf0_raw, (FA_LDS char*)vbuf1_raw, (FA_LDS char*)vbuf2_raw,
+                               (FA_LDS char*)vbuf3_raw};
   // block-sparse: the key tiles visible to any of the workgroup's query blocks, in order, with one
   // flag bit per query block (two tiles per mask block)
   __shared__ uint16_t tlist_raw[SPARSE ? 2 * kMaxMaskBlocks : 1];
@@ -313,7 +323,8 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
 
   // Step t: tile t (stage t % NS) must have landed; the next NS - 2 tiles may still be in flight.
   // After the barrier every wave is done with tile t-1, whose stage receives tile t + NS - 1.
-  constexpr int NS = kDqStages;
+  constexpr int NS = dq_stages<D>();
+  constexpr int G = dq_group<D>();
   auto step = [&](auto stage, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     if (NS > 2 && t + 1 < ntiles) wait_vmem_n<(NS - 2) * 2 * LOADS>();
@@ -325,8 +336,25 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
     }
     if (t < n_wave && mine(t)) tile(tix(t), kst[S], vst[S]);
   };
+  // Groups of G tiles (G > 1): tiles t .. t+G-1 in stages SB .. SB+G-1 (SB = 0 or G) must have
+  // landed; after the barrier every wave is done with the previous group, whose stages receive tiles
+  // t+G .. t+2G-1.
+  auto group = [&](auto sbase, int t) __attribute__((always_inline)) {
+    constexpr int SB = decltype(sbase)::value;
+    wait_vmem();
+    barrier();
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
+    for (int i = 0; i < G; ++i)
+      if (t + G + i < ntiles) {
+        load_tile(rK, t + G + i, kst[(SB + G + i) % NS]);
+        load_tile(rV, t + G + i, vst[(SB + G + i) % NS]);
+      }
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (t + i < n_wave && mine(t + i)) tile(tix(t + i), kst[SB + i], vst[SB + i]);
+  };
+#pragma unroll
+  for (int i = 0; i < (G > 1 ? G : NS - 1); ++i)
     if (i < ntiles) {
       load_tile(rK, i, kst[i]);
       load_tile(rV, i, vst[i]);
@@ -345,13 +373,21 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2 % NS>;
   int t = 0;
-  for (; t + NS - 1 < ntiles; t += NS) {
-    step(S0{}, t);
-    step(S1{}, t + 1);
-    if constexpr (NS > 2) step(S2{}, t + 2);
+  if constexpr (G > 1) {
+    using SG = std::integral_constant<int, G % NS>;
+    for (; t < ntiles; t += 2 * G) {
+      group(S0{}, t);
+      if (t + G < ntiles) group(SG{}, t + G);
+    }
+  } else {
+    for (; t + NS - 1 < ntiles; t += NS) {
+      step(S0{}, t);
+      step(S1{}, t + 1);
+      if constexpr (NS > 2) step(S2{}, t + 2);
+    }
+    if (t < ntiles) step(S0{}, t);
+    if (NS > 2 && t + 1 < ntiles) step(S1{}, t + 1);
   }
-  if (t < ntiles) step(S0{}, t);
-  if (NS > 2 && t + 1 < ntiles) step(S1{}, t + 1);
 
   // ---- epilogue: dQ = scale acc (bf16, RNE); lane holds query `query`, d = 32 dt + 8 gq + 4 half + 0..3.
   // A store of this layout would write 8-byte pieces of 32 rows per instruction; instead each wave
