@@ -48,5 +48,8 @@ def test_as_tiled_bytes_matches_a_brute_force_tile_count():
         assert got["fwd_bf16_kernel"] == 2 * rows * rb + 4 * rows + kv
         kvq = _brute_kv_tiles(N, causal, N, 256) * 64 * 2 * rb * 6
         assert got["bwd_dq_kernel"] == 4 * rows * rb + 12 * rows + kvq
-        qrows = sum(sum(1 for q in range(N) if not causal or q >= k0) for k0 in range(0, N, 128)) * 6
-        assert got["bwd_dkdv_kernel"] == 4 * rows * rb + qrows * (2 * rb + 8)
+        bk = 256 if d == 128 else 128  # keys per workgroup of the dK/dV kernel that runs
+        name = "bwd_dkdv_kl_kernel" if d == 128 else "bwd_dkdv_kernel"
+        assert bench.dkdv_kernel(w) == name
+        qrows = sum(sum(1 for q in range(N) if not causal or q >= k0) for k0 in range(0, N, bk)) * 6
+        assert got[name] == 4 * rows * rb + qrows * (2 * rb + 8)
