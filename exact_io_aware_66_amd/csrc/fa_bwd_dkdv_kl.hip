@@ -9,8 +9,8 @@
 // registers and 8 waves (two per SIMD) share a compute unit.  Per tile: S = Q K^T and
 // dP - D = dO V^T - D (v_mfma_f32_32x32x16_bf16, dP starting from -D), P = exp2(S scale log2 e -
 // LSE log2 e), dS = P (dP - D), packed to bf16, then dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T
-// through transposing LDS reads), query halves in order; the other wave of the SIMD fills the gaps
-// between a wave's phases.  Query tiles of 32 rows stream through a four-stage LDS ring fetched three
+// through transposing LDS reads), query halves in order, P and dS of the second half computed beside
+// the first half's products; the other wave of the SIMD fills the gaps between a wave's phases.  Query tiles of 32 rows stream through a four-stage LDS ring fetched three
 // tiles ahead, one barrier per tile.  NOTE-005: FlashAttention, "Method" (the recomputation of the
 // attention block in the backward).
 #include <type_traits>
@@ -170,18 +170,20 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
         cf = 1.f;
       }
       const FA_LDS float* lse_t = (const FA_LDS float*)(st + 2 * QTILE);
+      f32x4 l4[4];
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 l4 = *(const FA_LDS f32x4*)(lse_t + 8 * gq + 4 * half);
+      for (int gq = 0; gq < 2; ++gq) l4[gq] = *(const FA_LDS f32x4*)(lse_t + 8 * gq + 4 * half);
+      auto unit = [&](int r) {
+        const float pr_ = fast_exp2(fmaf(s[r], cf, -l4[r >> 2][r & 3]));
+        dp[r] = pr_ * dp[r];
+        s[r] = pr_;
+      };
+      // the first query half (elements 0..7) before the dV/dK products; the second beside the first
+      // half's products, which do not need it
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * gq + e;
-          const float pr_ = fast_exp2(fmaf(s[r], cf, -l4[e]));
-          dp[r] = pr_ * dp[r];
-          s[r] = pr_;
-        }
-      }
-      const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8), db0 = pack8(dp, 0), db1 = pack8(dp, 8);
+      for (int r = 0; r < 8; ++r) unit(r);
+      const bf16x8 pb0 = pack8(s, 0), db0 = pack8(dp, 0);
+      bf16x8 pb1, db1;
 
       // dV^T += dO^T P, dK^T += Q^T dS: (ks, dt) steps, query half ks outermost; A operands through
       // the transposing read, one step ahead
@@ -201,6 +203,18 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
         const int dt = i % DT;
         dvt[dt] = mfma32x32x16(bd[i & 1], i < DT ? pb0 : pb1, dvt[dt]);
         dkt[dt] = mfma32x32x16(bq[i & 1], i < DT ? db0 : db1, dkt[dt]);
+        if (i == 0) {  // (read here rather than above, which would not fit the registers)
+          l4[2] = *(const FA_LDS f32x4*)(lse_t + 16 + 4 * half);
+          l4[3] = *(const FA_LDS f32x4*)(lse_t + 24 + 4 * half);
+        }
+        if (i < DT) {  // elements 8..15, two per step of the first half
+          unit(8 + 2 * i);
+          unit(9 + 2 * i);
+          if (i == DT - 1) {
+            pb1 = pack8(s, 8);
+            db1 = pack8(dp, 8);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
