@@ -557,7 +557,7 @@ hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, 
 #ifndef FA_DKDV_KL
 #define FA_DKDV_KL 1
 #endif
-  if (FA_DKDV_KL && p.d == 128 && !p.dropout && p.block_mask == nullptr)
+  if (FA_DKDV_KL && p.d == 128 && p.block_mask == nullptr)
     return launch_dkdv_kl_bf16(p, q, k, v, dO, lse2, delta, dk, dv);
   return p.d == 64 ? launch_dkdv_d<64>(p, q, k, v, dO, lse2, delta, dk, dv)
                    : launch_dkdv_d<128>(p, q, k, v, dO, lse2, delta, dk, dv);

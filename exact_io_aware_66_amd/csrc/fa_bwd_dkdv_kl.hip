@@ -1,6 +1,6 @@
-// dK and dV of the backward at d = 128 for dense attention without dropout, with two waves per SIMD:
-// the arithmetic of bwd_dkdv_kernel (fa_bwd_bf16.hip) in the same order, so the results are bitwise
-// the same, with K held in LDS instead of registers.
+// dK and dV of the backward at d = 128 for attention without a block mask (dense, and with fused
+// dropout), with two waves per SIMD: the arithmetic of bwd_dkdv_kernel (fa_bwd_bf16.hip) in the same
+// order, so the results are bitwise the same, with K held in LDS instead of registers.
 //
 // A wave of bwd_dkdv_kernel keeps K and V of its 32 keys, dK^T and dV^T and two sets of S and dP in
 // about 400 registers, one wave per SIMD.  Here K of the workgroup's 256 keys sits in LDS (64 KiB,
@@ -10,9 +10,14 @@
 // dP - D = dO V^T - D (v_mfma_f32_32x32x16_bf16, dP starting from -D), P = exp2(S scale log2 e -
 // LSE log2 e), dS = P (dP - D), packed to bf16, then dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T
 // through transposing LDS reads), query halves in order, P and dS of the second half computed beside
-// the first half's products; the other wave of the SIMD fills the gaps between a wave's phases.  Query tiles of 32 rows stream through a four-stage LDS ring fetched three
-// tiles ahead, one barrier per tile.  NOTE-005: FlashAttention, "Method" (the recomputation of the
-// attention block in the backward).
+// the first half's products; the other wave of the SIMD fills the gaps between a wave's phases.
+// Query tiles of 32 rows stream through a four-stage LDS ring fetched three tiles ahead, one barrier
+// per tile.  With dropout, the keep decisions of each 32 x 32 block are regenerated as in
+// bwd_dkdv_kernel (one Philox call per lane in the generator's query-major layout, a byte transpose
+// through the wave's LDS block); the dropout instantiations keep part of their state in scratch
+// memory, the others none.  NOTE-005: FlashAttention, "Method" (the recomputation of the attention
+// block in the backward); dropout: promptingindex page, "Why attention is memory-bound, not
+// compute-bound" (dropout among the steps of the attention chain).
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -26,7 +31,7 @@ constexpr int kKeysKl = 32;           // keys per wave
 constexpr int kBcKl = kWkl * kKeysKl;  // 256 keys per workgroup
 constexpr int kBrKl = 32;             // query rows per tile
 
-template <bool CAUSAL, bool PADDED>
+template <bool CAUSAL, bool PADDED, bool DROP>
 __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16* __restrict__ Q,
                                                                    const __bf16* __restrict__ K,
                                                                    const __bf16* __restrict__ V,
@@ -35,7 +40,8 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
                                                                    const float* __restrict__ NDELTA,
                                                                    __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                                    int H, int N, float scale, float c_log2,
-                                                                   const int32_t* __restrict__ seqlens, int BH) {
+                                                                   const int32_t* __restrict__ seqlens, Dropout dr,
+                                                                   int BH) {
   constexpr int D = 128;
   constexpr int DS = D / 16;                     // k-steps over d
   constexpr int DT = D / 32;                     // 32-wide d tiles
@@ -47,6 +53,7 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
   __shared__ __attribute__((aligned(1024))) char st1_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2_raw[STAGE];
   __shared__ __attribute__((aligned(1024))) char st3_raw[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t drop_raw[DROP ? kWkl * 1024 : 16];
   const FA_LDS char* const kst = (const FA_LDS char*)kst_raw;
 
   const int lane = threadIdx.x & 63;
@@ -130,6 +137,20 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
     auto step = [&](auto mask, const FA_LDS char* st, int u) __attribute__((always_inline)) {
       // S = Q K^T and dP - D = dO V^T - D: A operands Q, dO rows l32 at d = 16 ds + 8 half, B operand
       // K from LDS (row 32 wave + l32); fragments read one k-step ahead
+      // Dropout keep words of tile u in this kernel's layout (lane = key, the 16 queries of its half): each
+      // lane draws the words of one query (the generator's layout), writes the bytes key-major into the
+      // wave's LDS block and reads back the 4 words of its own key
+      u32x4 kwt = {};
+      if constexpr (DROP) {
+        FA_LDS uint8_t* mt = (FA_LDS uint8_t*)drop_raw + wave * 1024;
+        const u32x4 w = dropout_words(dr, (uint32_t)bh, (it0 + u) * kBrKl + l32, kw / 32, half);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mt[(8 * g + 4 * half + e) * 32 + l32] = (uint8_t)(w[g] >> (8 * e));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) kwt[g] = *(const FA_LDS uint32_t*)(mt + l32 * 32 + 8 * g + 4 * half);
+      }
       f32x16 s = zero16();
       f32x16 dp;
       {
@@ -139,6 +160,7 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
         dp = __builtin_shufflevector(__builtin_shufflevector(a, b4, 0, 1, 2, 3, 4, 5, 6, 7),
                                      __builtin_shufflevector(c, d4, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5, 6, 7, 8,
                                      9, 10, 11, 12, 13, 14, 15);
+        if constexpr (DROP) dp *= (float)dr.t * (1.f / 256.f);
       }
       bf16x8 fq[2], fd[2], fk[2];
       auto rd = [&](int ds) {
@@ -170,13 +192,23 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
         cf = 1.f;
       }
       const FA_LDS float* lse_t = (const FA_LDS float*)(st + 2 * QTILE);
-      f32x4 l4[4];
+      f32x4 l4[4], nd4[DROP ? 4 : 1];
 #pragma unroll
-      for (int gq = 0; gq < 2; ++gq) l4[gq] = *(const FA_LDS f32x4*)(lse_t + 8 * gq + 4 * half);
+      for (int gq = 0; gq < 2; ++gq) {
+        l4[gq] = *(const FA_LDS f32x4*)(lse_t + 8 * gq + 4 * half);
+        if constexpr (DROP) nd4[gq] = *(const FA_LDS f32x4*)(lse_t + 64 + 8 * gq + 4 * half);
+      }
       auto unit = [&](int r) {
         const float pr_ = fast_exp2(fmaf(s[r], cf, -l4[r >> 2][r & 3]));
-        dp[r] = pr_ * dp[r];
-        s[r] = pr_;
+        float dpv = dp[r];  // dP - D (dropout: dP - D t / 256)
+        float pv = pr_;     // P for dV: the kept probabilities (their 256/t scale is applied to dV at the end)
+        if constexpr (DROP) {
+          const bool keep = dropout_keep(dr, kwt[r >> 2], r & 3);
+          dpv = keep ? dpv * dr.scale : nd4[r >> 2][r & 3];  // (256 / t) dP - D, or 0 - D
+          pv = keep ? pr_ : 0.f;
+        }
+        dp[r] = pr_ * dpv;
+        s[r] = pv;
       };
       // the first query half (elements 0..7) before the dV/dK products; the second beside the first
       // half's products, which do not need it
@@ -206,6 +238,10 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
         if (i == 0) {  // (read here rather than above, which would not fit the registers)
           l4[2] = *(const FA_LDS f32x4*)(lse_t + 16 + 4 * half);
           l4[3] = *(const FA_LDS f32x4*)(lse_t + 24 + 4 * half);
+        }
+        if constexpr (DROP) {  // -D of the second half, each group read just before its elements
+          if (i == 0) nd4[2] = *(const FA_LDS f32x4*)(lse_t + 64 + 16 + 4 * half);
+          if (i == 2) nd4[3] = *(const FA_LDS f32x4*)(lse_t + 64 + 24 + 4 * half);
         }
         if (i < DT) {  // elements 8..15, two per step of the first half
           unit(8 + 2 * i);
@@ -299,7 +335,7 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kx[e] = live ? dkt[dt][4 * gq + e] * scale : 0.f;
-          vx[e] = live ? dvt[dt][4 * gq + e] : 0.f;
+          vx[e] = live ? dvt[dt][4 * gq + e] * (DROP ? dr.scale : 1.f) : 0.f;
         }
         *(FA_LDS bf16x4*)(ep + tile_off<D>(l32, d0)) = pack4(kx[0], kx[1], kx[2], kx[3]);
         *(FA_LDS bf16x4*)(ep + VB + tile_off<D>(l32, d0)) = pack4(vx[0], vx[1], vx[2], vx[3]);
@@ -320,27 +356,35 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
   }
 }
 
-template <bool CAUSAL, bool PADDED>
+template <bool CAUSAL, bool PADDED, bool DROP>
 hipError_t launch_kl(const Problem& p, const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                      const float* ndelta, void* dk, void* dv) {
   const int nkb = (p.N + kBcKl - 1) / kBcKl;
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL((bwd_dkdv_kl_kernel<CAUSAL, PADDED>), dim3((unsigned)(nkb * BH)), dim3(kWkl * 64), 0, p.stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, ndelta,
-                     (__bf16*)dk, (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, BH);
+  const Dropout dr{p.drop_k0, p.drop_k1, p.drop_off2, p.drop_t, 256.f / (float)p.drop_t};
+  hipLaunchKernelGGL((bwd_dkdv_kl_kernel<CAUSAL, PADDED, DROP>), dim3((unsigned)(nkb * BH)), dim3(kWkl * 64), 0,
+                     p.stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse2, ndelta,
+                     (__bf16*)dk, (__bf16*)dv, p.H, p.N, p.scale, p.scale * kLog2e, p.seqlens, dr, BH);
   return hipGetLastError();
+}
+
+template <bool DROP>
+hipError_t launch_kl_m(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
+                       const float* lse2, const float* ndelta, void* dk, void* dv) {
+  const bool pad = p.seqlens != nullptr;
+  if (p.causal)
+    return pad ? launch_kl<true, true, DROP>(p, q, k, v, dO, lse2, ndelta, dk, dv)
+               : launch_kl<true, false, DROP>(p, q, k, v, dO, lse2, ndelta, dk, dv);
+  return pad ? launch_kl<false, true, DROP>(p, q, k, v, dO, lse2, ndelta, dk, dv)
+             : launch_kl<false, false, DROP>(p, q, k, v, dO, lse2, ndelta, dk, dv);
 }
 
 }  // namespace
 
 hipError_t launch_dkdv_kl_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                                const float* lse2, const float* ndelta, void* dk, void* dv) {
-  const bool pad = p.seqlens != nullptr;
-  if (p.causal)
-    return pad ? launch_kl<true, true>(p, q, k, v, dO, lse2, ndelta, dk, dv)
-               : launch_kl<true, false>(p, q, k, v, dO, lse2, ndelta, dk, dv);
-  return pad ? launch_kl<false, true>(p, q, k, v, dO, lse2, ndelta, dk, dv)
-             : launch_kl<false, false>(p, q, k, v, dO, lse2, ndelta, dk, dv);
+  return p.dropout ? launch_kl_m<true>(p, q, k, v, dO, lse2, ndelta, dk, dv)
+                   : launch_kl_m<false>(p, q, k, v, dO, lse2, ndelta, dk, dv);
 }
 
 }  // namespace fa

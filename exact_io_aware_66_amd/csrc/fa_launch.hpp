@@ -51,8 +51,8 @@ hipError_t launch_bwd_prepare(const Problem& p, bool bf16, const void* o, const 
                               void* workspace);
 hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                                 void* dk, void* dv, const void* workspace);
-// dK/dV at d = 128 for dense attention without dropout with K in LDS and two waves per SIMD (bitwise
-// the results of the general kernel; lse2: LSE log2(e), ndelta: -D, both from the workspace).
+// dK/dV at d = 128 without a block mask (dense or with dropout) with K in LDS and two waves per SIMD
+// (bitwise the results of the general kernel; lse2: LSE log2(e), ndelta: -D, both from the workspace).
 hipError_t launch_dkdv_kl_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* dO,
                                const float* lse2, const float* ndelta, void* dk, void* dv);
 // With p.pre_o set, the dQ pass also writes D and LSE log2(e) of its rows into the workspace, bitwise equal

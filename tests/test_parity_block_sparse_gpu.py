@@ -67,7 +67,8 @@ def test_block_sparse_long_causal_local(fa):
     assert not fails, fails
 
 
-@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("fp32", 64, True)])
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 128, False), ("bf16", 64, False),
+                                           ("fp32", 64, True)])
 def test_all_visible_mask_is_the_dense_result_bitwise(fa, dtype, d, causal):
     N = 520
     x = workloads.draw_custom(2, 2, N, d, dtype=dtype, causal=causal, seqlens=[N, 301], seed=8)

@@ -73,7 +73,8 @@ def test_dropout_long_causal(fa):
     assert not fails, fails
 
 
-@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("fp32", 64, True)])
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 128, False), ("bf16", 64, False),
+                                           ("fp32", 64, True)])
 def test_zero_dropout_is_dense_bitwise(fa, dtype, d, causal):
     x = workloads.draw_custom(2, 2, 333, d, dtype=dtype, causal=causal, seqlens=[333, 200], seed=6)
     dense = run_gpu(fa, x)
