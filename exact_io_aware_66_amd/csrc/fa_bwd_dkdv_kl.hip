@@ -135,8 +135,6 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
     // One tile u from stage st.  MASK: the masked form (std::true_type, std::false_type, or a run-time
     // bool for the tiles near the causal diagonal, where the form differs between waves).
     auto step = [&](auto mask, const FA_LDS char* st, int u) __attribute__((always_inline)) {
-      // S = Q K^T and dP - D = dO V^T - D: A operands Q, dO rows l32 at d = 16 ds + 8 half, B operand
-      // K from LDS (row 32 wave + l32); fragments read one k-step ahead
       // Dropout keep words of tile u in this kernel's layout (lane = key, the 16 queries of its half): each
       // lane draws the words of one query (the generator's layout), writes the bytes key-major into the
       // wave's LDS block and reads back the 4 words of its own key
@@ -151,6 +149,8 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
 #pragma unroll
         for (int g = 0; g < 4; ++g) kwt[g] = *(const FA_LDS uint32_t*)(mt + l32 * 32 + 8 * g + 4 * half);
       }
+      // S = Q K^T and dP - D = dO V^T - D: A operands Q, dO rows l32 at d = 16 ds + 8 half, B operand
+      // K from LDS (row 32 wave + l32); fragments read one k-step ahead
       f32x16 s = zero16();
       f32x16 dp;
       {
