@@ -20,6 +20,7 @@ from parity_util import run_gpu
 pytestmark = pytest.mark.gpu
 
 BF16_WORKLOADS = [2, 3, 4]
+LONG = BF16_WORKLOADS + [5]  # with N = 65536 (its gradient sums are checked beside its parity test)
 
 
 def _say(msg):
@@ -38,7 +39,7 @@ def _visible(B, N, causal, seqlens, dev):
     return vis
 
 
-@pytest.mark.parametrize("wid", BF16_WORKLOADS)
+@pytest.mark.parametrize("wid", LONG)
 def test_rows_of_p_sum_to_one(fa, wid):
     """sum_j exp(S_ij - LSE_i) = 1 on sampled rows of every (b, h), S recomputed in fp32 from the
     bf16 inputs.  The kernel's LSE sums bf16-rounded probabilities: round to nearest with 8
@@ -67,7 +68,7 @@ def test_rows_of_p_sum_to_one(fa, wid):
     assert worst <= 2.0 ** -8 + 1e-4
 
 
-@pytest.mark.parametrize("wid", BF16_WORKLOADS)
+@pytest.mark.parametrize("wid", LONG)
 def test_output_in_convex_hull(fa, wid):
     """min_j V_jc <= O_ic <= max_j V_jc over the visible keys j, up to O's bf16 rounding (half an ulp,
     2^-8 relative) and fp32 slack: the weights P_ij / l_i the kernel applies are an exact convex
@@ -95,7 +96,7 @@ def test_output_in_convex_hull(fa, wid):
     assert float(over.max()) == 0.0
 
 
-@pytest.mark.parametrize("wid", BF16_WORKLOADS)
+@pytest.mark.parametrize("wid", LONG)
 def test_constant_values_give_constant_output(fa, wid):
     """V_j = v for every key j: O_i = v exactly in bf16 (the fp32 result differs from v by sums'
     rounding, ~1e-6 relative, far below half a bf16 ulp), and dS = P (dO.v - dO.O) vanishes up to
@@ -136,7 +137,7 @@ def test_gradient_sums(fa, wid):
     assert e_k <= 1e-3 * dk_mag and e_v <= 1e-3 * dv_mag
 
 
-@pytest.mark.parametrize("wid", [1] + BF16_WORKLOADS)
+@pytest.mark.parametrize("wid", [1] + LONG)
 def test_scale_folding_is_bitwise(fa, wid):
     """(2 q, scale / 2) against (q, scale): O, LSE, dK and dV bit for bit equal, dQ exactly halved."""
     w = workloads.WORKLOADS[wid]
