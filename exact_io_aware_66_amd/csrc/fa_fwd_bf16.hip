@@ -14,7 +14,9 @@
 //     each other's stalls.  Dense d = 128: one workgroup of 8 waves (256 query rows) per compute
 //     unit, so each K/V tile reaches the unit's LDS once for 256 rows.  d = 64 and block-sparse
 //     masks: workgroups of 4 waves (128 rows, the mask's block), two per compute unit (measured:
-//     the 8-wave form is 3 % faster at d = 128 and 3-7 % slower at d = 64);
+//     the 8-wave form is 3 % faster at d = 128 and 3-7 % slower at d = 64); dense d = 64 without
+//     dropout: three per compute unit (a wave within 168 registers, K and V^T fragments read one
+//     step ahead; measured: -7 % forward time at N = 1024, -1 % at N = 65536);
 //   * Q of the wave stays in registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16);
 //     each lane holds one query column of the score tile, so the row max/sum are in-lane (the two
 //     lane halves hold different keys of the same queries and are combined once, at the end);
@@ -62,7 +64,7 @@ constexpr float kLazyRescale = 8.0f;                 // base-2 headroom before t
 // to bf16 on its way into LDS, P V as in the bf16 path; the per-tensor descales of Q and K are folded
 // into c_log2 and that of V into o_scale.
 template <int D, bool CAUSAL, bool PADDED, bool NEG, bool SPARSE, bool DROP, bool F8>
-__global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SPARSE>())) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), ((D == 64 && !SPARSE && !DROP) ? 3 : 8 / fwd_waves<D, SPARSE>())) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int H, int N, float c_log2,
                                                           const int32_t* __restrict__ seqlens,
@@ -293,7 +295,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
               : fmaxf(fmaxf(ext, v[r]), fmaxf(v[r + 1], fmaxf(v[r + 2], v[r + 3])));
   };
 
-  // S^T(tile in kb) = K Q^T into s[set]: DS k-steps of 2 MFMAs, K fragments read two k-steps ahead;
+  // S^T(tile in kb) = K Q^T into s[set]: DS k-steps of 2 MFMAs, K fragments read KRA k-steps ahead;
   // `between(ds)` places VALU work after the MFMAs of k-step ds
   auto scores = [&](int set, const FA_LDS char* kb, auto&& between) __attribute__((always_inline)) {
     if constexpr (F8) {
@@ -324,15 +326,16 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
-    bf16x8 kf[3][2];
+    constexpr int KRA = (D == 64) ? 1 : 2;  // K fragments read KRA k-steps ahead
+    bf16x8 kf[KRA + 1][2];
     auto rd = [&](int ds, bf16x8 (&f)[2]) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) f[kt] = lds_read_b128(kb, tile_off<D>(32 * kt + l32, 16 * ds + 8 * half));
     };
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[set][kt] = zero16();
-    rd(0, kf[0]);
-    rd(1, kf[1]);
+#pragma unroll
+    for (int ds = 0; ds < KRA; ++ds) rd(ds, kf[ds]);
     // Raised issue priority while this wave feeds S to the matrix cores, so that of two waves on a SIMD in
     // different phases the one with score products goes first (measured: -3 % forward at d = 64,
     // N = 65536, where the two workgroups of a compute unit drift apart; no change elsewhere).
@@ -340,9 +343,9 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       __builtin_amdgcn_sched_barrier(0);
-      if (ds + 2 < DS) rd(ds + 2, kf[(ds + 2) % 3]);
+      if (ds + KRA < DS) rd(ds + KRA, kf[(ds + KRA) % (KRA + 1)]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[set][kt] = mfma32x32x16(kf[ds % 3][kt], qf[ds], s[set][kt]);
+      for (int kt = 0; kt < 2; ++kt) s[set][kt] = mfma32x32x16(kf[ds % (KRA + 1)][kt], qf[ds], s[set][kt]);
       between(ds);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -352,28 +355,29 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
   // O^T += V^T P^T over the tile in vb, k-step outermost: 4 DT MFMAs.  V^T fragment of product i
   // (dt = i % DT, ks = i / DT): lane (d = 32 dt + l32, half) needs keys 16 ks + 4 half + 0..3 and
   // 16 ks + 8 + 4 half + 0..3, the key order of pn; two transposing reads supply them (bases for
-  // rows vrow and vrow + 8, compile-time offsets of 16 rows).  The fragments run two products ahead
-  // in a ring of three; the first two are read by the caller during the score products before it
+  // rows vrow and vrow + 8, compile-time offsets of 16 rows).  The fragments run VRA products ahead
+  // in a ring of VRA + 1; the first VRA are read by the caller during the score products before it
   // (pv_head), so the matrix cores do not wait for them at the phase change.  `between(i)` follows
   // MFMA i.
   constexpr int NPV = 4 * DT;
-  bf16x8 vf[3];
+  constexpr int VRA = (D == 64) ? 1 : 2;  // V^T fragments read VRA products ahead
+  bf16x8 vf[VRA + 1];
   auto pv_rd = [&](const FA_LDS char* vb, int i) __attribute__((always_inline)) {
     const int ks = i / DT, dt = i % DT;
     const uint32_t off0 = tile_off<D>(vrow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
     const uint32_t off8 = tile_off<D>(vrow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
-    vf[i % 3] = cat(lds_read_tr(vb, off0), lds_read_tr(vb, off8));
+    vf[i % (VRA + 1)] = cat(lds_read_tr(vb, off0), lds_read_tr(vb, off8));
   };
   auto pv_head = [&](const FA_LDS char* vb) __attribute__((always_inline)) {
-    pv_rd(vb, 0);
-    pv_rd(vb, 1);
+#pragma unroll
+    for (int i = 0; i < VRA; ++i) pv_rd(vb, i);
   };
   auto pv = [&](const FA_LDS char* vb, auto&& between) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < NPV) pv_rd(vb, i + 2);
-      acc[i % DT] = mfma32x32x16(vf[i % 3], pn[i / DT], acc[i % DT]);
+      if (i + VRA < NPV) pv_rd(vb, i + VRA);
+      acc[i % DT] = mfma32x32x16(vf[i % (VRA + 1)], pn[i / DT], acc[i % DT]);
       between(i);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -383,14 +387,15 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), (8 / fwd_waves<D, SP
   // scaled to the base-2 domain in place; raise the maximum to the tile's.  Returns the factor O and
   // l must be multiplied by (1 when the maximum is unchanged).
   auto mask_update = [&](int set, int t) -> float {
-    const int key0 = tix(t) * kFwdBc;
+    // element (kt, r) holds key key0 + 32 kt + 8 (r / 4) + 4 half + r % 4: visible iff its offset
+    // 32 kt + 8 (r / 4) + r % 4, a constant per register, is below one per-lane limit
+    const int lim = (CAUSAL ? min(L, query + 1) : L) - (tix(t) * kFwdBc + 4 * half);
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = (key < L) & (!CAUSAL | (key <= query));
+        const bool vis = (32 * kt + 8 * (r >> 2) + (r & 3)) < lim;
         const float v = vis ? s[set][kt][r] * c_log2 : -INFINITY;
         s[set][kt][r] = v;
         mx = fmaxf(mx, v);
