@@ -251,14 +251,25 @@ struct Dropout {
   float scale;      // 256 / t
 };
 
+// a ^ b ^ k in one instruction (v_bitop3_b32, truth table 0x96 = three-input XOR; the compiler emits
+// two v_xor_b32 for it); k is wave-uniform (a scalar register written by scalar instructions)
+__device__ __forceinline__ uint32_t xor3_vvs(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// X3: the three-input XORs as single instructions (fewer instructions, but an opaque statement the
+// register allocator cannot move; used where registers are not the limit)
+template <bool X3 = false>
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = X3 ? xor3_vvs((uint32_t)(p1 >> 32), c1, k0) : (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = X3 ? xor3_vvs((uint32_t)(p0 >> 32), c3, k1) : (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -270,8 +281,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 }
 
 // The four keep words of (query i, 32-key block jb, half h): byte e of word g is key 8 g + 4 h + e.
+template <bool X3 = false>
 __device__ __forceinline__ u32x4 dropout_words(const Dropout& dr, uint32_t bh, int i, int jb, int h) {
-  return philox4x32_10((uint32_t)i, (uint32_t)jb, bh, dr.off2 + (uint32_t)h, dr.k0, dr.k1);
+  return philox4x32_10<X3>((uint32_t)i, (uint32_t)jb, bh, dr.off2 + (uint32_t)h, dr.k0, dr.k1);
 }
 
 __device__ __forceinline__ bool dropout_keep(const Dropout& dr, uint32_t word, int e) {

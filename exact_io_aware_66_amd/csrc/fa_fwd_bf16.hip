@@ -270,7 +270,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), ((D == 64 && !SPARSE
   // 256/t scale of the kept ones is applied to O in the epilogue).
   u32x4 kwd = {};
   auto dunit = [&](int t, int kt) {
-    if constexpr (DROP) kwd = dropout_words(dr, (uint32_t)bh, query, 2 * tix(t) + kt, half);
+    if constexpr (DROP) kwd = dropout_words<true>(dr, (uint32_t)bh, query, 2 * tix(t) + kt, half);
   };
   auto punit = [&](int set, int ks, int e, float cf) {
     const int kt = ks >> 1, r = 8 * (ks & 1) + 2 * e;
