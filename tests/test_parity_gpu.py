@@ -86,6 +86,34 @@ def test_workload5_sampled(fa):
     assert not fails, fails
 
 
+def test_long_causal_d128_sampled(fa):
+    """N = 16384, d = 128, causal, q_std = 4 (the long-sequence shape at the larger head size: 64 key
+    blocks of 256 per head, each with its diagonal tiles): O, LSE and dQ on sampled rows, dK and dV on
+    sampled keys (their oracle needs LSE and D of all 16384 rows, one fp64 pass per head, computed
+    here), block edges included."""
+    N, H = 16384, 2
+    x = workloads.draw_custom(1, H, N, 128, dtype="bf16", causal=True, q_std=4.0, seed=16384)
+    _say(f"[parity] long causal N={N} d=128 H={H}: sampled rows and keys")
+    got = run_gpu(fa, x)
+    g = torch.Generator().manual_seed(5)
+    edges = [0, 1, 31, 32, 255, 256, 257, 4095, 4096, N - 257, N - 256, N - 2, N - 1]
+    pick = lambda: torch.unique(torch.cat([torch.tensor(edges), torch.randint(0, N, (51,), generator=g)]))
+    dt = x["q"].dtype
+    report, fails = [], []
+    for h in range(H):
+        rows, keys = pick(), pick()
+        o_r, lse_r = oracle.forward_rows(x["q"], x["k"], x["v"], x["scale"], True, None, 0, h, rows)
+        dq_r = oracle.backward_rows(x["q"], x["k"], x["v"], x["do"], x["scale"], True, None, 0, h, rows)
+        lse, D = oracle.row_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], True, None, 0, h, chunk=2048)
+        dk_r, dv_r = oracle.backward_keys(x["q"], x["k"], x["v"], x["do"], x["scale"], True, None, 0, h, keys, lse, D)
+        for name, gt, ref in (("o", got["o"][0, h, rows], o_r), ("lse", got["lse"][0, h, rows], lse_r),
+                              ("dq", got["dq"][0, h, rows], dq_r), ("dk", got["dk"][0, h, keys], dk_r),
+                              ("dv", got["dv"][0, h, keys], dv_r)):
+            fails += check(f"{name}[h{h}]", gt[None], ref[None], dt, name, report)
+    _say("\n".join(report))
+    assert not fails, fails
+
+
 TAILS = [1, 17, 100, 129, 300, 1000]
 
 
