@@ -25,6 +25,9 @@
 //                  first-half queries first, interleaved with P and dS of the second half.
 //             Tiles with hidden pairs (causal diagonal, key padding, ragged tail) set the hidden
 //             scores to -inf first (so P = 0 and dS = 0 there).
+// At d = 128 without a block mask (dense, or with dropout) the dK/dV pass runs bwd_dkdv_kl_kernel
+// (fa_bwd_dkdv_kl.hip) instead: the same arithmetic in the same order with K in LDS, so that two
+// waves share each SIMD; bwd_dkdv_kernel serves d = 64 and the block-sparse masks.
 // dQ comes from a query-block-outer kernel of its own (fa_bwd_dq.hip), so that every output row has
 // exactly one writer and no atomic additions are needed anywhere in the backward.
 #include <type_traits>
