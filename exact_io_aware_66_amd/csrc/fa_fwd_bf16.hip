@@ -326,7 +326,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), ((D == 64 && !SPARSE
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
-    constexpr int KRA = (D == 64) ? 1 : 2;  // K fragments read KRA k-steps ahead
+    constexpr int KRA = 1;  // K fragments read KRA k-steps ahead
     bf16x8 kf[KRA + 1][2];
     auto rd = [&](int ds, bf16x8 (&f)[2]) {
 #pragma unroll
@@ -360,7 +360,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), ((D == 64 && !SPARSE
   // (pv_head), so the matrix cores do not wait for them at the phase change.  `between(i)` follows
   // MFMA i.
   constexpr int NPV = 4 * DT;
-  constexpr int VRA = (D == 64) ? 1 : 2;  // V^T fragments read VRA products ahead
+  constexpr int VRA = (D == 64) ? 1 : 3;  // V^T fragments read VRA products ahead
   bf16x8 vf[VRA + 1];
   auto pv_rd = [&](const FA_LDS char* vb, int i) __attribute__((always_inline)) {
     const int ks = i / DT, dt = i % DT;
