@@ -243,20 +243,21 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
         dp = ndel16;
       }
     }
-    bf16x8 fk[3], fv[3];
+    constexpr int RRA = D == 128 ? 1 : 2;  // K/V row fragments read RRA k-steps ahead
+    bf16x8 fk[RRA + 1], fv[RRA + 1];
     auto rd = [&](int ds, bf16x8& k, bf16x8& v) {
       const uint32_t off = tile_off<D>(32 * kt + l32, 16 * ds + 8 * half);
       k = lds_read_b128(kb, off);
       v = lds_read_b128(vb, off);
     };
-    rd(0, fk[0], fv[0]);
-    rd(1, fk[1], fv[1]);
+#pragma unroll
+    for (int ds = 0; ds < RRA; ++ds) rd(ds, fk[ds], fv[ds]);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       __builtin_amdgcn_sched_barrier(0);
-      if (ds + 2 < DS) rd(ds + 2, fk[(ds + 2) % 3], fv[(ds + 2) % 3]);
-      s = mfma32x32x16(fk[ds % 3], qf[ds], s);
-      dp = mfma32x32x16(fv[ds % 3], gf[ds], dp);
+      if (ds + RRA < DS) rd(ds + RRA, fk[(ds + RRA) % (RRA + 1)], fv[(ds + RRA) % (RRA + 1)]);
+      s = mfma32x32x16(fk[ds % (RRA + 1)], qf[ds], s);
+      dp = mfma32x32x16(fv[ds % (RRA + 1)], gf[ds], dp);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -299,20 +300,21 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
 
     // dQ^T += K^T dS^T: K^T fragment (lane: d = 32 dt + l32; keys 16 ks + 4 half + 0..3 and
     // 16 ks + 8 + 4 half + 0..3) from two transposing reads (bases for rows trow and trow + 8)
-    bf16x8 fa[3];
+    constexpr int TRA = D == 128 ? 3 : 2;  // K^T fragments read TRA products ahead
+    bf16x8 fa[TRA + 1];
     auto rdk = [&](int i, bf16x8& a) {
       const int dt = i >> 1, ks = 2 * kt + (i & 1);
       const uint32_t b0 = tile_off<D>(trow, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
       const uint32_t b8 = tile_off<D>(trow + 8, 32 * dt + 16 * (g & 1) + 4 * (j & 3)) + ks * 16 * D * 2;
       a = cat(lds_read_tr(kb, b0), lds_read_tr(kb, b8));
     };
-    rdk(0, fa[0]);
-    rdk(1, fa[1]);
+#pragma unroll
+    for (int i = 0; i < TRA; ++i) rdk(i, fa[i]);
 #pragma unroll
     for (int i = 0; i < 2 * DT; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < 2 * DT) rdk(i + 2, fa[(i + 2) % 3]);
-      acc[i >> 1] = mfma32x32x16(fa[i % 3], dsb[i & 1], acc[i >> 1]);
+      if (i + TRA < 2 * DT) rdk(i + TRA, fa[(i + TRA) % (TRA + 1)]);
+      acc[i >> 1] = mfma32x32x16(fa[i % (TRA + 1)], dsb[i & 1], acc[i >> 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
