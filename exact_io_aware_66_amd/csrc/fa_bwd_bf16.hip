@@ -42,15 +42,18 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerWave = 32;
 constexpr int kBwdBc = kBwdWaves * kBwdKeysPerWave;  // 128 keys per workgroup
 #ifndef FA_BWD_READ_AHEAD
-#define FA_BWD_READ_AHEAD 2
+#define FA_BWD_READ_AHEAD 0
 #endif
 #ifndef FA_BWD_READ_AHEAD_B
-#define FA_BWD_READ_AHEAD_B 2
+#define FA_BWD_READ_AHEAD_B 0
 #endif
 // LDS operand fragments are read this many MFMA steps ahead: row reads (score phase) and
-// transposing reads (dV/dK phase)
-constexpr int kRA = FA_BWD_READ_AHEAD;
-constexpr int kRB = FA_BWD_READ_AHEAD_B;
+// transposing reads (dV/dK phase); 0 selects the measured choice per head size (d = 64: one and
+// three, -0.5 to -1.4 % dK/dV time against two and two; d = 128: two and two)
+template <int D>
+constexpr int bwd_ra() { return FA_BWD_READ_AHEAD > 0 ? FA_BWD_READ_AHEAD : D == 64 ? 1 : 2; }
+template <int D>
+constexpr int bwd_rb() { return FA_BWD_READ_AHEAD_B > 0 ? FA_BWD_READ_AHEAD_B : D == 64 ? 3 : 2; }
 
 // ---------------------------------------------------------------------------------------------
 // -D_i = -sum_c dO_ic O_ic and (bf16 path) LSE_i log2(e).  D/8 threads per row.  The workspace keeps
@@ -97,6 +100,8 @@ __global__ __launch_bounds__(256, bwd_wg_per_cu<D>()) void bwd_dkdv_kernel(const
                                                           __bf16* __restrict__ dV, int H, int N, float scale,
                                                           float c_log2, const int32_t* __restrict__ seqlens,
                                                           const uint8_t* __restrict__ bmask, Dropout dr, int BH) {
+  constexpr int kRA = bwd_ra<D>();
+  constexpr int kRB = bwd_rb<D>();
   constexpr int BR = bwd_rows_per_tile<D>();  // query rows per tile
   constexpr int QS = BR / 32;                 // 32-row halves of a tile
   constexpr int CH = D / 8;                   // 16-byte chunks per row
