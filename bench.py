@@ -525,7 +525,7 @@ def main():
                          "byte counters of a profiler run, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the attention of one "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); the attention of one "
               f"(batch, head) never crosses GPUs and no multi-GPU path exists", file=sys.stderr)
         sys.exit(2)
 
