@@ -43,7 +43,8 @@ def _compare(x, got, report):
 
 
 CASES = [(300, 64, "none", "bf16", 0.2), (300, 128, "causal", "bf16", 0.5), (1000, 64, "causal+pad", "bf16", 0.1),
-         (1000, 128, "pad", "bf16", 0.3), (129, 128, "causal", "bf16", 0.7), (300, 64, "causal+pad", "fp32", 0.2),
+         (1000, 128, "pad", "bf16", 0.3), (129, 128, "causal", "bf16", 0.7), (1000, 128, "causal+pad", "bf16", 0.2),
+         (300, 64, "causal+pad", "fp32", 0.2),
          (200, 128, "none", "fp32", 0.5)]
 
 
