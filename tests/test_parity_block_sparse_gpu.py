@@ -30,7 +30,7 @@ CASES = [  # (N, d, mask, dtype, pattern)
     (300, 64, "none", "bf16", "random"), (300, 128, "causal", "bf16", "random"),
     (1000, 64, "causal+pad", "bf16", "random"), (1000, 128, "pad", "bf16", "random"),
     (1000, 128, "causal", "bf16", "local+global"), (700, 64, "causal", "bf16", "local"),
-    (1000, 128, "causal+pad", "bf16", "random"),
+    (1000, 128, "causal+pad", "bf16", "random"), (500, 64, "pad", "bf16", "random"), (700, 128, "none", "bf16", "random"),
     (300, 64, "causal+pad", "fp32", "random"), (260, 128, "none", "fp32", "random"),
 ]
 

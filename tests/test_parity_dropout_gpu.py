@@ -44,6 +44,7 @@ def _compare(x, got, report):
 
 CASES = [(300, 64, "none", "bf16", 0.2), (300, 128, "causal", "bf16", 0.5), (1000, 64, "causal+pad", "bf16", 0.1),
          (1000, 128, "pad", "bf16", 0.3), (129, 128, "causal", "bf16", 0.7), (1000, 128, "causal+pad", "bf16", 0.2),
+         (500, 64, "causal", "bf16", 0.3), (500, 64, "pad", "bf16", 0.4), (700, 128, "none", "bf16", 0.15),
          (300, 64, "causal+pad", "fp32", 0.2),
          (200, 128, "none", "fp32", 0.5)]
 
