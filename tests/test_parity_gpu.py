@@ -154,10 +154,14 @@ def test_empty_and_clamped_lengths(fa, d):
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.3])
 @pytest.mark.parametrize("d", [64, 128])
-def test_unusual_scales(fa, scale, d):
-    x = workloads.draw_custom(1, 2, 300, d, dtype="bf16", causal=True, seed=5)
+@pytest.mark.parametrize("mask", ["causal", "pad", "none"])
+def test_unusual_scales(fa, scale, d, mask):
+    """scale < 0 selects the minimum-tracking forms of the forward (every mask form); scale 0 gives
+    uniform weights over the visible keys."""
+    seqlens = [137] if mask == "pad" else None
+    x = workloads.draw_custom(1, 2, 300, d, dtype="bf16", causal=mask == "causal", seqlens=seqlens, seed=5)
     x["scale"] = scale
-    _say(f"[parity] scale={scale} d={d} N=300")
+    _say(f"[parity] scale={scale} d={d} N=300 mask={mask}")
     got = run_gpu(fa, x)
     report = []
     fails = _compare_full(x, got, report)
