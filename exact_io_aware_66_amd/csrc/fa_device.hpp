@@ -151,9 +151,27 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
 // compiler does not track the asynchronous LDS write: it would otherwise wait for every
 // outstanding load (vmcnt(0)) before reads of an unrelated LDS stage.  The caller orders the
 // transfer with wait_vmem / wait_vmem_n and a barrier before any wave reads the destination.
+//
+// FA_POISON_LDS (a debug build, libfa_poison.so): each lane first fills its own destination bytes
+// with all-ones words (NaN in bf16, fp32 and FP8 E4M3) and waits for that store, so that a wave
+// reading a stage before the transfer has landed, or after the stage was handed to the next tile,
+// reads NaN instead of plausible stale data; correctly synchronised kernels give results bitwise
+// equal to the release build.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: no compiler-generated code here relies on it
+__device__ __forceinline__ void poison_lds(const FA_LDS void* lds_base, int bytes_per_lane) {
+#ifdef FA_POISON_LDS
+  FA_LDS char* const p = (FA_LDS char*)const_cast<FA_LDS void*>(lds_base) + bytes_per_lane * (threadIdx.x & 63);
+  if (bytes_per_lane == 16) *(volatile FA_LDS u32x4*)p = u32x4{~0u, ~0u, ~0u, ~0u};
+  else *(volatile FA_LDS uint32_t*)p = ~0u;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)lds_base;
+  (void)bytes_per_lane;
+#endif
+}
 __device__ __forceinline__ void bload_lds16(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
+  poison_lds(lds_base, 16);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base))
@@ -161,6 +179,7 @@ __device__ __forceinline__ void bload_lds16(u32x4 r, uint32_t voff, const FA_LDS
 }
 // 4 bytes at byte offset voff of the buffer into LDS at (wave-uniform) lds_base + 4 * lane.
 __device__ __forceinline__ void bload_lds4(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
+  poison_lds(lds_base, 4);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base))

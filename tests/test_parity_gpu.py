@@ -251,10 +251,10 @@ def test_no_device_allocation(fa):
 @pytest.mark.parametrize("B,H,N,causal", [(1, 40, 1000, True), (1, 40, 1000, False), (2, 36, 500, True),
                                           (2, 16, 4096, True)])
 def test_dkdv_batched_equals_per_head(fa, B, H, N, causal):
-    """dK and dV of a many-head problem (several key blocks per compute unit, XCD-grouped order) equal
-    bit for bit those of each head run as a problem of its own (one key block per workgroup, a
-    different grid and order): each key block's result depends only on its own inputs.  Head (0, 0)
-    is also checked against the oracle."""
+    """O, LSE, dQ, dK and dV of a many-head problem (several blocks per compute unit, XCD-grouped
+    order) equal bit for bit those of each head run as a problem of its own (a different grid and
+    workgroup order): each block's result depends only on its own inputs.  Head (0, 0) is also
+    checked against the oracle."""
     x = workloads.draw_custom(B, H, N, 128, dtype="bf16", causal=causal, seed=2000 + N + H)
     _say(f"[parity] dK/dV batched vs per head B={B} H={H} N={N} causal={causal}")
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
@@ -267,6 +267,11 @@ def test_dkdv_batched_equals_per_head(fa, B, H, N, causal):
     for b in range(B):
         for h in range(H):
             sl = [t[b:b + 1, h:h + 1].contiguous() for t in (q, k, v, o, do)]
+            o1, lse1 = torch.empty_like(sl[0]), torch.empty(1, 1, N, dtype=torch.float32, device="cuda")
+            fa.fa_forward(*sl[:3], o1, lse1, x["scale"], causal)
+            torch.cuda.synchronize()
+            assert torch.equal(o1[0, 0], o[b, h]), ("o", b, h)
+            assert torch.equal(lse1[0, 0], lse[b, h]), ("lse", b, h)
             g = [torch.empty_like(sl[0]) for _ in range(3)]
             fa.fa_backward(*sl, lse[b:b + 1, h:h + 1].contiguous(), *g, x["scale"], causal, None, ws1)
             torch.cuda.synchronize()
