@@ -179,13 +179,20 @@ def test_high_dynamic_range_rescaling(fa):
     assert not fails, fails
 
 
-def test_determinism(fa):
-    x = workloads.draw_custom(2, 4, 777, 128, dtype="bf16", causal=True, seed=3)
-    _say("[parity] determinism x3")
-    runs = [run_gpu(fa, x) for _ in range(3)]
-    for name in ("o", "lse", "dq", "dk", "dv"):  # single writer per element, fixed summation order
-        for r in runs[1:]:
-            assert torch.equal(r[name], runs[0][name]), name
+@pytest.mark.parametrize("d,extra", [(128, None), (64, None), (128, "dropout"), (64, "sparse")])
+def test_determinism(fa, d, extra):
+    """20 runs bitwise identical (single writer per element, fixed summation order)."""
+    x = workloads.draw_custom(2, 4, 777, d, dtype="bf16", causal=True, seed=3)
+    if extra == "dropout":
+        x["dropout"] = (0.1, 77, 0)
+    if extra == "sparse":
+        x["block_mask"] = workloads.draw_block_mask(2, 4, 777, "random", density=0.5, window=1, seed=3)
+    _say(f"[parity] determinism x20 d={d} {extra or 'dense'}")
+    first = run_gpu(fa, x)
+    for _ in range(19):
+        r = run_gpu(fa, x)
+        for name in ("o", "lse", "dq", "dk", "dv"):
+            assert torch.equal(r[name], first[name]), name
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
