@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, bwd_wg_per_cu<D>()) void bwd_dkdv_kernel(const
   // ---- work item: (key block, batch*head); key block 0 has the most query tiles under the causal
   // mask, so ascending rank is heaviest first.  All key blocks of a head go to one XCD when B*H is
   // a multiple of 8 (its Q and dO rows then stay in that XCD's L2).
-  const int wid = blockIdx.x;
+  const int wid = work_item();
   int kblock, bh;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;

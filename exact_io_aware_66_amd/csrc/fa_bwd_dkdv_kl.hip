@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kWkl * 64, 1) void bwd_dkdv_kl_kernel(const __bf16*
 
   // ---- work item: (block of 256 keys, batch*head), ascending key blocks first (heaviest under the
   // causal mask); all key blocks of a head on one XCD when B*H is a multiple of 8
-  const int wid = blockIdx.x;
+  const int wid = work_item();
   int kblock, bh;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;

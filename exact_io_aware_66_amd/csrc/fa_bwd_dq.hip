@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kDqWaves * 64, kDqWaves == 8 ? 1 : 2) void bwd_dq_k
   const int half = lane >> 5;
 
   // ---- work item: (query block, batch*head), heaviest first, XCD-local heads
-  const int wid = blockIdx.x;
+  const int wid = work_item();
   int rank, bh;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;

@@ -170,6 +170,17 @@ __device__ __forceinline__ void poison_lds(const FA_LDS void* lds_base, int byte
   (void)bytes_per_lane;
 #endif
 }
+// The work item of this workgroup: its id in the grid, or (FA_POISON_LDS debug build) the ids in
+// reverse order, so that every item runs on other compute units, in another order and beside other
+// items than in the release build; each output element has one writer and a fixed summation order,
+// so the results must not change.
+__device__ __forceinline__ int work_item() {
+#ifdef FA_POISON_LDS
+  return (int)(gridDim.x - 1 - blockIdx.x);
+#else
+  return (int)blockIdx.x;
+#endif
+}
 __device__ __forceinline__ void bload_lds16(u32x4 r, uint32_t voff, const FA_LDS void* lds_base) {
   poison_lds(lds_base, 16);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"

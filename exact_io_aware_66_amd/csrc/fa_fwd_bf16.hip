@@ -97,7 +97,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, SPARSE>()), ((D == 64 && !SPARSE
   const int half = lane >> 5;
 
   // ---- work item: (query block, batch*head), heaviest first, XCD-local heads
-  const int wid = blockIdx.x;
+  const int wid = work_item();
   int rank, bh;
   if ((BH & 7) == 0) {
     const int hpx = BH >> 3;

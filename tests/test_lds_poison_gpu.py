@@ -3,11 +3,13 @@ libfa.so by the same build step).
 
 In that build every direct-to-LDS tile load first fills its destination with NaN words and waits for
 that store.  A wave that read a stage before its transfer had landed, or after the stage had been
-handed to the next tile, would then read NaN rather than plausible stale data; with correct waits
-and barriers the results are bitwise those of the release build.  Every instantiation family that
-loads through LDS is run: the forward (dense, causal, padded, dropout, block-sparse, FP8), the dQ
-pass and both dK/dV kernels (the K-in-LDS one at d = 128, the general one at d = 64 and for block
-masks), at ragged sizes and at the long causal workload's full size.
+handed to the next tile, would then read NaN rather than plausible stale data.  The build also takes
+its work items in reverse workgroup order (other compute units, another order, other neighbours).
+With correct waits and barriers, and one writer per output element, the results are bitwise those
+of the release build.  Every instantiation family that loads through LDS is run: the forward (dense,
+causal, padded, dropout, block-sparse, FP8), the dQ pass and both dK/dV kernels (the K-in-LDS one at
+d = 128, the general one at d = 64 and for block masks), at ragged sizes and at the long causal
+workload's full size.
 """
 import os
 
