@@ -35,6 +35,15 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_poison_build_exports_the_same_symbols():
+    """The LDS-poison debug library (built beside libfa.so) offers the same C ABI."""
+    path = os.path.join(os.path.dirname(os.path.abspath(fa.__file__)), "libfa_poison.so")
+    assert os.path.exists(path), "libfa_poison.so is not built; run exact_io_aware_66_amd/build.py"
+    dbg = ctypes.CDLL(path)
+    for name in fa.EXPORTS:
+        assert hasattr(dbg, name), name
+
+
 def test_status_strings(lib):
     for code, name in fa.STATUS.items():
         assert lib.fa_status_string(code).decode() == name
